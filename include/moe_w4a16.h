@@ -1,0 +1,213 @@
+/*
+ * moe_w4a16.h - C ABI of libmoe_w4a16.so, a routed-expert mixture-of-experts
+ * layer with W4A16 group-32 expert weights for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one tuned across a 512-expert, top-10, hidden-2560 model on
+ * the pages "[Model][SM70] Adapt Qwen3.8 Flash Next NVFP4" (section
+ * "Implemented route": the (2560, 640, 512, top-10) routed-expert geometry) and
+ * "[Perf][SM70] Narrow Qwen3.8 AWQ active grouped decode" (section "Purpose":
+ * AWQ W4A16 with effective group size 32, a grouped operator over active
+ * experts, multi-row active-expert segments with offsets-based scheduling, and
+ * scratch buffers the operator mutates).  One layer call is, in order:
+ *
+ *   moe_route              softmax over expert logits, top-k, renormalise
+ *   moe_permute            token->expert permutation: segments and offsets
+ *   moe_w4a16_grouped_ffn  dequant-fused gate/up GEMM, SiLU(gate)*up, down GEMM
+ *   moe_combine            router-weighted sum back to token order
+ *
+ * Conventions for every entry point
+ *   - Pointers to tensors are DEVICE pointers unless stated otherwise; fp16
+ *     tensors are passed as uint16_t bit patterns.  Every non-null tensor
+ *     pointer must be 16-byte aligned.  All tensors are dense, row-major.
+ *   - Ownership: the caller allocates and frees every buffer, including the
+ *     workspaces.  The library never allocates or frees memory, never
+ *     synchronises, keeps no mutable global state and may be called from
+ *     several host threads at once.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream) and runs asynchronously.  A call that returns MOE_OK has
+ *     only enqueued its kernels.
+ *   - Errors: arguments are validated on the host before anything is enqueued;
+ *     on a non-OK return nothing was enqueued, except MOE_ERR_HIP, which
+ *     reports a failed launch (the library reads and clears hipGetLastError,
+ *     so a pending error left by earlier unrelated work is reported too).
+ *   - T == 0 is valid: the call returns MOE_OK, enqueues nothing and writes
+ *     nothing; tensor pointers may then be NULL.
+ *   - Device-side preconditions that are documented but not checked: logits
+ *     are finite; expert ids are in [0, E) and distinct within a token (what
+ *     moe_route produces); routing tensors passed to a later call are the
+ *     unmodified outputs of the earlier calls of the same layer.
+ *   - Results are deterministic: no step depends on the order in which
+ *     threads or workgroups run, so a repeated call gives identical bits.
+ *
+ * Shapes.  T tokens, E experts, top_k experts per token, S = T * top_k slots
+ * (slot s = t * top_k + j is the j-th choice of token t), hidden size H,
+ * intermediate size I, group size 32 along the reduction dim K.
+ *
+ * Weight layout (N = output rows, K = reduction dim, G = K / 32):
+ *   qweight int32 [E, N, K/8]   nibble j (bits 4j..4j+3) of word w is k = 8w+j
+ *   scales  fp16  [E, N, G]
+ *   qzeros  int32 [E, N/8, G]   nibble j of word w is row n = 8w+j
+ *   dequantised weight  W[e, n, k] = (q - z[e, n, k/32]) * scales[e, n, k/32]
+ * w13 has N = 2I, K = H (rows [0, I) gate, [I, 2I) up); w2 has N = H, K = I.
+ *
+ * Limits: 1 <= E <= 4096; 1 <= top_k <= min(E, 64); S < 2^31; group_size == 32;
+ * H and I multiples of 32 with 32 <= H, I <= 16384.
+ */
+#ifndef MOE_W4A16_H_
+#define MOE_W4A16_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes of every entry point. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1 /* null/misaligned pointer, bad shape or count   */
+#define MOE_ERR_UNSUPPORTED 2 /* valid but outside the limits (group_size...)  */
+#define MOE_ERR_WORKSPACE 3   /* workspace_bytes below the size query's result */
+#define MOE_ERR_HIP 4         /* a kernel launch failed                        */
+
+/* Static, NUL-terminated description of a return code (host only). */
+const char* moe_status_string(int status);
+
+/* Library ABI version, MAJOR * 100 + MINOR. */
+int moe_abi_version(void);
+
+/*
+ * moe_route - router softmax, top-k and renormalisation.
+ *
+ * For every token t: p = softmax(logits[t, :]); the top_k experts with the
+ * largest logits are chosen in rank order (equal logits: lower expert index
+ * first); weights[t, j] = p[id_j] / sum_j' p[id_j'].  Ranking is done on the
+ * fp32 logits themselves, so the ids are exact.  The full-softmax denominator
+ * cancels in the renormalisation and is not formed.
+ * Source: the routed-expert top-10 geometry on "[Model][SM70] Adapt Qwen3.8
+ * Flash Next NVFP4", section "Implemented route".
+ *
+ *   logits        in   fp32  [T, E]
+ *   topk_ids      out  int32 [T, top_k]   expert ids in rank order
+ *   topk_weights  out  fp32  [T, top_k]   sum to 1 per token
+ */
+int moe_route(const float* logits, int64_t T, int32_t E, int32_t top_k,
+              int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* Workspace bytes moe_permute needs for these sizes (0 when T <= 64). */
+size_t moe_permute_workspace_bytes(int64_t T, int32_t top_k, int32_t E);
+
+/*
+ * moe_permute - stable token-to-expert permutation: active-expert segments and
+ * their offsets ("multi-row active-expert segments and offsets-based
+ * scheduling", "[Perf][SM70] Narrow Qwen3.8 AWQ active grouped decode",
+ * section "Purpose").
+ *
+ * Sorted row r belongs to expert e iff expert_offsets[e] <= r <
+ * expert_offsets[e+1]; the rows of one expert are its slots in ascending slot
+ * order.
+ *
+ *   topk_ids        in   int32 [T, top_k]
+ *   expert_offsets  out  int32 [E + 1]   offsets[0] = 0, offsets[E] = S
+ *   sorted_slots    out  int32 [S]       slot held by sorted row r
+ *   slot_rows       out  int32 [S]       sorted row of slot s (inverse)
+ *   active_experts  out  int32 [E]       experts with >= 1 row, ascending,
+ *                                        then -1 up to E
+ *   num_active      out  int32 [1]       number of active experts
+ *   workspace       scratch, device, >= moe_permute_workspace_bytes(...)
+ *                   bytes (may be NULL when that size is 0); contents on
+ *                   entry are ignored.
+ */
+int moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
+                int32_t* expert_offsets, int32_t* sorted_slots,
+                int32_t* slot_rows, int32_t* active_experts,
+                int32_t* num_active, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Workspace bytes the expert FFN entry points need for these sizes. */
+size_t moe_ffn_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H,
+                               int32_t I);
+
+/*
+ * moe_w4a16_grouped_ffn - dequant-fused grouped expert FFN over the active
+ * experts (the AWQ "active-stage" grouped W4A16 operator of "[Perf][SM70]
+ * Narrow Qwen3.8 AWQ active grouped decode", section "Purpose"; W4A16 group
+ * size 32 per "[Model][SM70] Support Qwen3.8 Flash Next with PLE offload",
+ * section "SM70 QSA prefill tuning").
+ *
+ * For every sorted row r of expert e, with token t = sorted_slots[r] / top_k:
+ *   h = x[t, :] . W13[e]^T                (2I values)
+ *   a = SiLU(h[0:I]) * h[I:2I]            (I values, SiLU(v) = v / (1 + e^-v))
+ *   y_sorted[r, :] = a . W2[e]^T          (H values)
+ * Weights are dequantised exactly as (q - z) and scaled per 32-wide group in
+ * fp32; x . W is accumulated in fp32 and a is carried to the down product at
+ * about 22 bits of precision.  The kernel variant (bandwidth-bound decode
+ * GEMV for T <= 8, matrix-core grouped GEMM otherwise) is chosen from T.
+ *
+ *   x                 in   fp16  [T, H]
+ *   expert_offsets, sorted_slots, active_experts, num_active: moe_permute's
+ *                     outputs for the same routing
+ *   w13_qweight/scales/qzeros   in  W13 [E, 2I, H] in the layout above
+ *   w2_qweight/scales/qzeros    in  W2  [E, H, I]  in the layout above
+ *   group_size        must be 32
+ *   y_sorted          out  fp32  [S, H]  per-row expert outputs, sorted order
+ *   workspace         scratch, device, >= moe_ffn_workspace_bytes(...) bytes;
+ *                     contents on entry are ignored.  Two calls that overlap
+ *                     in time must not share a workspace.
+ */
+int moe_w4a16_grouped_ffn(
+    const uint16_t* x, int64_t T, int32_t top_k, const int32_t* expert_offsets,
+    const int32_t* sorted_slots, const int32_t* active_experts,
+    const int32_t* num_active, const int32_t* w13_qweight,
+    const uint16_t* w13_scales, const int32_t* w13_qzeros,
+    const int32_t* w2_qweight, const uint16_t* w2_scales,
+    const int32_t* w2_qzeros, int32_t E, int32_t H, int32_t I,
+    int32_t group_size, float* y_sorted, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/*
+ * moe_w4a16_gate_up / moe_w4a16_down - the two halves of
+ * moe_w4a16_grouped_ffn, for callers that schedule or time them apart.
+ * moe_w4a16_gate_up computes a = SiLU(h[0:I]) * h[I:2I] for every sorted row
+ * into the workspace; moe_w4a16_down reads it and writes y_sorted.  A down
+ * call must follow a gate_up call with the same routing, sizes and workspace,
+ * on the same stream.  Arguments are as for moe_w4a16_grouped_ffn.
+ */
+int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k,
+                      const int32_t* expert_offsets,
+                      const int32_t* sorted_slots,
+                      const int32_t* active_experts,
+                      const int32_t* num_active, const int32_t* w13_qweight,
+                      const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                      int32_t E, int32_t H, int32_t I, int32_t group_size,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
+                   const int32_t* active_experts, const int32_t* num_active,
+                   const int32_t* w2_qweight, const uint16_t* w2_scales,
+                   const int32_t* w2_qzeros, int32_t E, int32_t H, int32_t I,
+                   int32_t group_size, float* y_sorted, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine - router-weighted combine back to token order.
+ *
+ *   out[t, h] = fp16_rne( sum_{j = 0..top_k-1} topk_weights[t, j] *
+ *                          y_sorted[slot_rows[t * top_k + j], h] )
+ * summed in fp32 in ascending j, rounded to fp16 once (round to nearest
+ * even).  A gather without atomics.
+ *
+ *   y_sorted      in   fp32  [S, H]
+ *   topk_weights  in   fp32  [T, top_k]
+ *   slot_rows     in   int32 [S]
+ *   out           out  fp16  [T, H]
+ */
+int moe_combine(const float* y_sorted, const float* topk_weights,
+                const int32_t* slot_rows, int64_t T, int32_t top_k, int32_t H,
+                uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H_ */

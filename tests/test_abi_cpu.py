@@ -1,0 +1,126 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before touching
+the GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4a16_group_quantized_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4a16.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ops.LIB_PATH),
+                                reason="libmoe_w4a16.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_layer_calls():
+    names = _declared_functions()
+    for fn in ("moe_route", "moe_permute", "moe_w4a16_grouped_ffn", "moe_combine"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ops.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(_declared_functions()) == set(ops.EXPORTED)
+
+
+def test_status_strings_and_version():
+    lib = ops.load_library()
+    assert lib.moe_abi_version() == 100
+    for st in range(5):
+        assert len(ops.status_string(st)) > 0
+    assert ops.status_string(99) == "unknown status"
+
+
+def test_workspace_queries():
+    assert ops.permute_workspace_bytes(64, 10, 512) == 0  # one workgroup, no scratch
+    assert ops.permute_workspace_bytes(65, 10, 512) > 0
+    assert ops.permute_workspace_bytes(4096, 10, 512) >= 64 * 512 * 12
+    a = ops.ffn_workspace_bytes(8, 10, 512, 2560, 640)
+    b = ops.ffn_workspace_bytes(4096, 10, 512, 2560, 640)
+    assert a >= 2 * 80 * 640 * 2 and b >= 2 * 40960 * 640 * 2 and b > a
+    # invalid sizes report 0
+    assert ops.ffn_workspace_bytes(8, 10, 512, 2561, 640) == 0
+    assert ops.permute_workspace_bytes(8, 0, 512) == 0
+
+
+FAKE = 0x1000  # an aligned non-null value; never dereferenced because validation fails first
+
+
+def test_route_rejects_bad_arguments():
+    lib = ops.load_library()
+    assert lib.moe_route(None, 4, 8, 2, None, None, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, -1, 8, 2, FAKE, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 8, 9, FAKE, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 8, 0, FAKE, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 0, 1, FAKE, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 5000, 2, FAKE, FAKE, None) == ops.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(FAKE, 4, 512, 65, FAKE, FAKE, None) == ops.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(FAKE + 4, 4, 8, 2, FAKE, FAKE, None) == ops.MOE_ERR_INVALID_ARG  # misaligned
+    assert lib.moe_route(None, 0, 8, 2, None, None, None) == ops.MOE_OK  # T = 0: nothing to do
+    assert lib.moe_route(FAKE, 1 << 28, 512, 10, FAKE, FAKE, None) == ops.MOE_ERR_UNSUPPORTED
+
+
+def test_permute_rejects_bad_arguments():
+    lib = ops.load_library()
+    args = [FAKE] * 6
+    assert lib.moe_permute(FAKE, 100, 10, 512, *args[:5], None, 0, None) == ops.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(FAKE, 100, 10, 512, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                           None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(None, 0, 10, 512, None, None, None, None, None, None, 0, None) == ops.MOE_OK
+
+
+def _ffn(lib, T=8, k=10, E=512, H=2560, I=640, gs=32, ws_bytes=1 << 30, y=FAKE, x=FAKE):
+    p = [FAKE] * 10
+    return lib.moe_w4a16_grouped_ffn(x, T, k, *p[:4], *p[4:10], E, H, I, gs, y, FAKE, ws_bytes, None)
+
+
+def test_ffn_rejects_bad_arguments():
+    lib = ops.load_library()
+    assert _ffn(lib, gs=64) == ops.MOE_ERR_UNSUPPORTED
+    assert _ffn(lib, gs=128) == ops.MOE_ERR_UNSUPPORTED
+    assert _ffn(lib, H=2570) == ops.MOE_ERR_INVALID_ARG
+    assert _ffn(lib, I=650) == ops.MOE_ERR_INVALID_ARG
+    assert _ffn(lib, H=32768) == ops.MOE_ERR_UNSUPPORTED
+    assert _ffn(lib, ws_bytes=16) == ops.MOE_ERR_WORKSPACE
+    assert _ffn(lib, y=None) == ops.MOE_ERR_INVALID_ARG
+    assert _ffn(lib, x=FAKE + 8) == ops.MOE_ERR_INVALID_ARG
+    assert _ffn(lib, T=0, x=None, y=None) == ops.MOE_OK
+    assert _ffn(lib, k=11, E=10) == ops.MOE_ERR_INVALID_ARG
+
+
+def test_gate_up_and_down_reject_bad_arguments():
+    lib = ops.load_library()
+    p = [FAKE] * 8
+    assert lib.moe_w4a16_gate_up(FAKE, 8, 10, *p[:7], 512, 2560, 640, 16, FAKE, 1 << 30,
+                                 None) == ops.MOE_ERR_UNSUPPORTED
+    assert lib.moe_w4a16_gate_up(FAKE, 8, 10, *p[:7], 512, 2560, 640, 32, None, 1 << 30,
+                                 None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_w4a16_down(8, 10, *p[:6], 512, 2560, 640, 32, FAKE, FAKE, 8,
+                              None) == ops.MOE_ERR_WORKSPACE
+
+
+def test_combine_rejects_bad_arguments():
+    lib = ops.load_library()
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 8, 10, 2561, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(FAKE, FAKE, None, 8, 10, 2560, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 8, 0, 2560, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(None, None, None, 0, 10, 2560, None, None) == ops.MOE_OK
+
+
+def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(ops, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        ops.load_library(str(tmp_path / "nope.so"))

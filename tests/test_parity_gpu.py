@@ -1,0 +1,233 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bit-exact: top-k ids, expert offsets, sorted slots, slot rows, active experts
+and their count.  Floating point: fp16 layer output within max |err| <= 2e-2
+and relative RMS <= 1e-2 of the unrounded fp64 oracle (tests/parity.py), the
+fp32 router weights within 1e-6, and the fp32 per-row expert outputs within a
+relative RMS of 1e-4.
+
+Sizes: every named workload (at its full size; the two prefill workloads are
+checked on sampled tokens, whose outputs the oracle computes one by one, plus
+bit-exact routing over all tokens), token counts 0/1/2/8/9/127/128, and the
+degenerate cases (one expert, k = E, E not a multiple of 64, every token on
+one expert, tied logits, the largest E and k).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import assert_fp16_close
+from w4a16_group_quantized_amd import inputs as synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from w4a16_group_quantized_amd import ops
+
+    ops.load_library()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.nodeid}", flush=True)
+    yield
+
+
+def _run_layer(host, shape, dev):
+    from w4a16_group_quantized_amd import ops
+
+    w = ops.weights_to_device(host, dev)
+    logits = torch.from_numpy(host["logits"]).to(dev)
+    x = torch.from_numpy(host["x"]).to(dev)
+    layer = ops.MoELayer(shape.T, shape.E, shape.top_k, shape.H, shape.I, dev)
+    out = layer(logits, x, w)
+    torch.cuda.synchronize()
+    res = {
+        "topk_ids": layer.ids.cpu().numpy(),
+        "topk_weights": layer.weights.cpu().numpy(),
+        "y_sorted": layer.y_sorted.cpu().numpy(),
+        "out": out.cpu().numpy(),
+    }
+    for k, v in layer.perm.items():
+        res[k] = v.cpu().numpy()
+    res["num_active"] = int(res["num_active"][0])
+    return res
+
+
+def _assert_routing_exact(got, ref):
+    assert np.array_equal(got["topk_ids"], ref["topk_ids"]), "topk_ids"
+    np.testing.assert_allclose(got["topk_weights"], ref["topk_weights"], rtol=0, atol=1e-6)
+    for key in ("expert_offsets", "sorted_slots", "slot_rows", "active_experts"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert got["num_active"] == int(ref["num_active"]), "num_active"
+
+
+def _full_check(shape, seed, dev, host=None):
+    host = host if host is not None else synth.make_inputs(shape, seed)
+    ref = oracle.layer(host, shape.top_k)
+    got = _run_layer(host, shape, dev)
+    if shape.T == 0:  # nothing is computed or written; outputs are empty
+        assert got["topk_ids"].shape == (0, shape.top_k) and got["out"].shape == (0, shape.H)
+        return got, ref
+    _assert_routing_exact(got, ref)
+    yref = ref["y_sorted"]
+    yerr = np.sqrt(((got["y_sorted"] - yref) ** 2).sum() / max((yref ** 2).sum(), 1e-30))
+    assert yerr < 1e-4, f"y_sorted rel-RMS {yerr}"
+    assert_fp16_close(got["out"], ref["out"], f"{shape} seed {seed}")
+    return got, ref
+
+
+# --------------------------------------------------------------------------- #
+# the named workloads
+# --------------------------------------------------------------------------- #
+def test_tiny_workload(dev):
+    _full_check(synth.WORKLOADS["tiny_e8_k2_h256_i128_t4"], 0, dev)
+
+
+def test_decode_workload_full(dev):
+    _full_check(synth.WORKLOADS["decode_e512_k10_h2560_i640_t8"], 0, dev)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+def test_decode_shard_token_sweep(dev, T):
+    base = synth.WORKLOADS["decode_shard_e512_k10_h2560_i160_t8"]
+    _full_check(synth.MoEShape(base.E, base.top_k, base.H, base.I, T), 0, dev)
+
+
+def _sampled_check(shape, dev, n_sample=40, seed=0):
+    host = synth.make_inputs(shape, seed)
+    ids, w = oracle.route(host["logits"], shape.top_k)
+    perm = oracle.permute(ids, shape.E)
+    got = _run_layer(host, shape, dev)
+    ref = {"topk_ids": ids, "topk_weights": w, **perm}
+    _assert_routing_exact(got, ref)
+    rng = np.random.default_rng(1234)
+    tokens = np.unique(np.concatenate([[0, shape.T - 1], rng.choice(shape.T, n_sample, replace=False)]))
+    sub = oracle.token_outputs(host, ids, w, tokens)
+    assert_fp16_close(got["out"][tokens], sub, f"{shape} sampled {tokens.size} tokens")
+    return got, host, ids
+
+
+def test_prefill_workload_sampled(dev):
+    _sampled_check(synth.WORKLOADS["prefill_e512_k10_h2560_i640_t1024"], dev)
+
+
+def test_prefill_zipf_workload_sampled(dev):
+    shape = synth.WORKLOADS["prefill_zipf_e512_k10_h2560_i640_t4096"]
+    got, host, ids = _sampled_check(shape, dev)
+    # the skew is real: the hottest expert holds hundreds of rows
+    counts = np.diff(got["expert_offsets"])
+    assert counts.max() > 1000 and (counts == 0).sum() > 100
+
+
+# --------------------------------------------------------------------------- #
+# token counts and degenerate cases
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("T", [0, 1, 2, 8, 9, 63, 64, 65, 127, 128])
+def test_token_counts(dev, T):
+    _full_check(synth.MoEShape(E=64, top_k=6, H=512, I=256, T=T), T, dev)
+
+
+@pytest.mark.parametrize("E,k,H,I,T", [
+    (1, 1, 256, 128, 5),      # one expert, top-1: the dense FFN
+    (8, 8, 256, 128, 3),      # k = E: every expert on every token
+    (37, 5, 256, 96, 70),     # E not a multiple of 64, ragged I tile, > 64 tokens
+    (100, 3, 96, 32, 17),     # small odd geometry
+    (4096, 64, 64, 32, 3),    # largest E and top_k
+])
+def test_degenerate_shapes(dev, E, k, H, I, T):
+    _full_check(synth.MoEShape(E=E, top_k=k, H=H, I=I, T=T), 5, dev)
+
+
+def test_every_token_on_one_expert(dev):
+    shape = synth.MoEShape(E=32, top_k=4, H=256, I=128, T=200)
+    host = synth.make_inputs(shape, 9)
+    host["logits"][:, 7] += 100.0
+    got, ref = _full_check(shape, 9, dev, host)
+    assert np.all(got["topk_ids"][:, 0] == 7)
+    assert np.diff(got["expert_offsets"])[7] == shape.T
+
+
+def test_tied_logits(dev):
+    shape = synth.MoEShape(E=48, top_k=5, H=128, I=64, T=70)
+    host = synth.make_inputs(shape, 2)
+    host["logits"] = np.round(host["logits"], 0).astype(np.float32)  # many exact ties
+    host["logits"][3] = 0.5  # a fully tied row
+    host["logits"][4, :] = -0.0
+    host["logits"][4, ::2] = 0.0
+    got, ref = _full_check(shape, 2, dev, host)
+    assert got["topk_ids"][3].tolist() == [0, 1, 2, 3, 4]
+    assert got["topk_ids"][4].tolist() == [0, 1, 2, 3, 4]
+
+
+def test_repeat_calls_are_bitwise_identical(dev):
+    shape = synth.MoEShape(E=64, top_k=6, H=512, I=256, T=300)
+    host = synth.make_inputs(shape, 3)
+    a = _run_layer(host, shape, dev)
+    b = _run_layer(host, shape, dev)
+    for key in ("out", "y_sorted", "topk_weights", "sorted_slots"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+# --------------------------------------------------------------------------- #
+# single entry points in isolation
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("T,E", [(1, 1), (63, 7), (64, 512), (65, 512), (1000, 4096), (5000, 512)])
+def test_permute_alone_bit_exact(dev, T, E):
+    from w4a16_group_quantized_amd import ops
+
+    k = min(E, 10)
+    rng = np.random.default_rng(T + E)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    ref = oracle.permute(ids, E)
+    got = ops.moe_permute(torch.from_numpy(ids).to(dev), E)
+    torch.cuda.synchronize()
+    for key in ("expert_offsets", "sorted_slots", "slot_rows", "active_experts"):
+        assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+    assert int(got["num_active"].item()) == int(ref["num_active"])
+
+
+def test_combine_alone(dev):
+    from w4a16_group_quantized_amd import ops
+
+    T, k, H = 33, 7, 320
+    rng = np.random.default_rng(8)
+    y = rng.standard_normal((T * k, H)).astype(np.float32) * 20
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    slot_rows = rng.permutation(T * k).astype(np.int32)
+    ref = oracle.combine(y.astype(np.float64), w.astype(np.float64), slot_rows)
+    got = ops.moe_combine(torch.from_numpy(y).to(dev), torch.from_numpy(w).to(dev),
+                          torch.from_numpy(slot_rows).to(dev))
+    torch.cuda.synchronize()
+    assert_fp16_close(got.cpu().numpy(), ref, "combine")
+
+
+def test_gate_up_then_down_equals_grouped_ffn(dev):
+    from w4a16_group_quantized_amd import ops
+
+    shape = synth.MoEShape(E=64, top_k=6, H=512, I=256, T=8)
+    host = synth.make_inputs(shape, 11)
+    w = ops.weights_to_device(host, dev)
+    logits = torch.from_numpy(host["logits"]).to(dev)
+    x = torch.from_numpy(host["x"]).to(dev)
+    ids, wts = ops.moe_route(logits, shape.top_k)
+    perm = ops.moe_permute(ids, shape.E)
+    y_a = ops.moe_w4a16_grouped_ffn(x, shape.top_k, perm, w)
+    ws = torch.empty(ops.ffn_workspace_bytes(shape.T, shape.top_k, shape.E, shape.H, shape.I),
+                     dtype=torch.uint8, device=dev)
+    y_b = torch.empty_like(y_a)
+    ops.moe_w4a16_gate_up(x, shape.top_k, perm, w, ws)
+    ops.moe_w4a16_down(shape.T, shape.top_k, perm, w, y_b, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_a, y_b)

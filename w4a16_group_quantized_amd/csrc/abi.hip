@@ -1,0 +1,217 @@
+// C ABI of libmoe_w4a16.so: argument validation, workspace sizing and kernel
+// dispatch.  Declarations and the full contract are in include/moe_w4a16.h.
+// Nothing here allocates, frees or synchronises.
+#include <stdint.h>
+
+#include "../../include/moe_w4a16.h"
+#include "common.h"
+
+namespace {
+
+using namespace moe;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+int check_launch() {
+  const hipError_t err = hipGetLastError();
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// Routing sizes shared by every entry point.
+int check_routing(int64_t T, int32_t top_k, int32_t E) {
+  if (T < 0 || E < 1 || top_k < 1 || top_k > E) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts || top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (T * static_cast<int64_t>(top_k) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_dims(int32_t H, int32_t I, int32_t group_size) {
+  if (group_size != kGroup) return MOE_ERR_UNSUPPORTED;
+  if (H <= 0 || I <= 0 || H % kGroup || I % kGroup) return MOE_ERR_INVALID_ARG;
+  if (H / kGroup > kMaxGroups || I / kGroup > kMaxGroups) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe {
+
+size_t ffn_workspace_bytes(int64_t S, int E, int I) {
+  const size_t act = align256(static_cast<size_t>(S) * I * sizeof(uint16_t));
+  const size_t tiles = align256((static_cast<size_t>(S) + E + 1) * 2 * sizeof(int));
+  return 2 * act + tiles + 256;
+}
+
+FfnWorkspace ffn_workspace_carve(void* base, int64_t S, int E, int I) {
+  char* p = static_cast<char*>(base);
+  const size_t act = align256(static_cast<size_t>(S) * I * sizeof(uint16_t));
+  const size_t tiles = align256((static_cast<size_t>(S) + E + 1) * 2 * sizeof(int));
+  FfnWorkspace ws;
+  ws.act_hi = reinterpret_cast<uint16_t*>(p);
+  ws.act_lo = reinterpret_cast<uint16_t*>(p + act);
+  ws.tiles = reinterpret_cast<int*>(p + 2 * act);
+  ws.tile_count = reinterpret_cast<int*>(p + 2 * act + tiles);
+  return ws;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported size or group size";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than the size query requires";
+    case MOE_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_abi_version(void) { return 100; }
+
+int moe_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t* topk_ids,
+              float* topk_weights, void* stream) {
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(logits) || !ok_ptr(topk_ids) || !ok_ptr(topk_weights)) return MOE_ERR_INVALID_ARG;
+  launch_route(logits, static_cast<int>(T), E, top_k, topk_ids, topk_weights,
+               static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+size_t moe_permute_workspace_bytes(int64_t T, int32_t top_k, int32_t E) {
+  if (check_routing(T, top_k, E) != MOE_OK) return 0;
+  return permute_workspace_bytes(T, E);
+}
+
+int moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
+                int32_t* expert_offsets, int32_t* sorted_slots, int32_t* slot_rows,
+                int32_t* active_experts, int32_t* num_active, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(topk_ids) || !ok_ptr(expert_offsets) || !ok_ptr(sorted_slots) ||
+      !ok_ptr(slot_rows) || !ok_ptr(active_experts) || !ok_ptr(num_active))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = permute_workspace_bytes(T, E);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (need > 0 && !ok_ptr(workspace)) return MOE_ERR_INVALID_ARG;
+  launch_permute(topk_ids, static_cast<int>(T), top_k, E, expert_offsets, sorted_slots,
+                 slot_rows, active_experts, num_active, workspace,
+                 static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+size_t moe_ffn_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
+  if (check_routing(T, top_k, E) != MOE_OK || check_dims(H, I, kGroup) != MOE_OK) return 0;
+  return ffn_workspace_bytes(T * top_k, E, I);
+}
+
+int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t* expert_offsets,
+                      const int32_t* sorted_slots, const int32_t* active_experts,
+                      const int32_t* num_active, const int32_t* w13_qweight,
+                      const uint16_t* w13_scales, const int32_t* w13_qzeros, int32_t E, int32_t H,
+                      int32_t I, int32_t group_size, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (int st = check_dims(H, I, group_size)) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(expert_offsets) || !ok_ptr(sorted_slots) || !ok_ptr(active_experts) ||
+      !ok_ptr(num_active) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) || !ok_ptr(w13_qzeros) ||
+      !ok_ptr(workspace))
+    return MOE_ERR_INVALID_ARG;
+  const int64_t S = T * top_k;
+  if (workspace_bytes < ffn_workspace_bytes(S, E, I)) return MOE_ERR_WORKSPACE;
+  const FfnWorkspace ws = ffn_workspace_carve(workspace, S, E, I);
+  GateUpArgs a;
+  a.x = x;
+  a.T = static_cast<int>(T);
+  a.top_k = top_k;
+  a.E = E;
+  a.H = H;
+  a.I = I;
+  a.offsets = expert_offsets;
+  a.sorted_slots = sorted_slots;
+  a.active = active_experts;
+  a.num_active = num_active;
+  a.qw = w13_qweight;
+  a.sc = w13_scales;
+  a.qz = w13_qzeros;
+  launch_gate_up_decode(a, ws, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
+                   const int32_t* active_experts, const int32_t* num_active,
+                   const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros,
+                   int32_t E, int32_t H, int32_t I, int32_t group_size, float* y_sorted,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (int st = check_dims(H, I, group_size)) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(expert_offsets) || !ok_ptr(active_experts) || !ok_ptr(num_active) ||
+      !ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) || !ok_ptr(y_sorted) ||
+      !ok_ptr(workspace))
+    return MOE_ERR_INVALID_ARG;
+  const int64_t S = T * top_k;
+  if (workspace_bytes < ffn_workspace_bytes(S, E, I)) return MOE_ERR_WORKSPACE;
+  const FfnWorkspace ws = ffn_workspace_carve(workspace, S, E, I);
+  DownArgs a;
+  a.T = static_cast<int>(T);
+  a.top_k = top_k;
+  a.E = E;
+  a.H = H;
+  a.I = I;
+  a.offsets = expert_offsets;
+  a.active = active_experts;
+  a.num_active = num_active;
+  a.qw = w2_qweight;
+  a.sc = w2_scales;
+  a.qz = w2_qzeros;
+  a.y = y_sorted;
+  launch_down_decode(a, ws, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+int moe_w4a16_grouped_ffn(const uint16_t* x, int64_t T, int32_t top_k,
+                          const int32_t* expert_offsets, const int32_t* sorted_slots,
+                          const int32_t* active_experts, const int32_t* num_active,
+                          const int32_t* w13_qweight, const uint16_t* w13_scales,
+                          const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                          const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t E,
+                          int32_t H, int32_t I, int32_t group_size, float* y_sorted,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  // Validate everything before enqueuing either half.
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (int st = check_dims(H, I, group_size)) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) || !ok_ptr(y_sorted))
+    return MOE_ERR_INVALID_ARG;
+  if (int st = moe_w4a16_gate_up(x, T, top_k, expert_offsets, sorted_slots, active_experts,
+                                 num_active, w13_qweight, w13_scales, w13_qzeros, E, H, I,
+                                 group_size, workspace, workspace_bytes, stream))
+    return st;
+  return moe_w4a16_down(T, top_k, expert_offsets, active_experts, num_active, w2_qweight,
+                        w2_scales, w2_qzeros, E, H, I, group_size, y_sorted, workspace,
+                        workspace_bytes, stream);
+}
+
+int moe_combine(const float* y_sorted, const float* topk_weights, const int32_t* slot_rows,
+                int64_t T, int32_t top_k, int32_t H, uint16_t* out, void* stream) {
+  if (T < 0 || top_k < 1 || top_k > kMaxTopK) return top_k > kMaxTopK ? MOE_ERR_UNSUPPORTED
+                                                                        : MOE_ERR_INVALID_ARG;
+  if (T * static_cast<int64_t>(top_k) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (H <= 0 || H % kGroup) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(y_sorted) || !ok_ptr(topk_weights) || !ok_ptr(slot_rows) || !ok_ptr(out))
+    return MOE_ERR_INVALID_ARG;
+  launch_combine(y_sorted, topk_weights, slot_rows, static_cast<int>(T), top_k, H, out,
+                 static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Internal declarations shared by the HIP translation units of libmoe_w4a16.
+// Not part of the public ABI (see include/moe_w4a16.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 32;          // quantisation group size along K
+constexpr int kMaxExperts = 4096;   // E limit
+constexpr int kMaxTopK = 64;        // top_k limit (one router round per lane)
+constexpr int kMaxGroups = 512;     // K / 32 limit (K <= 16384)
+constexpr int kPermBlockTokens = 64;  // tokens per permutation block (one 64-bit mask)
+constexpr int kDecodeMaxT = 8;      // T at or below which the GEMV variant runs
+
+// ----------------------------------------------------------------------------
+// Launchers (each enqueues on `stream`, returns nothing; the ABI layer checks
+// hipGetLastError afterwards).
+// ----------------------------------------------------------------------------
+void launch_route(const float* logits, int T, int E, int top_k, int* ids,
+                  float* weights, hipStream_t stream);
+
+size_t permute_workspace_bytes(int64_t T, int E);
+void launch_permute(const int* ids, int T, int top_k, int E, int* offsets,
+                    int* sorted_slots, int* slot_rows, int* active,
+                    int* num_active, void* workspace, hipStream_t stream);
+
+struct FfnWorkspace {
+  uint16_t* act_hi;  // [S, I] fp16, high part of SiLU(gate)*up
+  uint16_t* act_lo;  // [S, I] fp16, act - act_hi rounded to fp16
+  int* tiles;        // matrix-core M-tile list (prefill variant)
+  int* tile_count;   // number of valid entries of `tiles`
+};
+size_t ffn_workspace_bytes(int64_t S, int E, int I);
+FfnWorkspace ffn_workspace_carve(void* base, int64_t S, int E, int I);
+
+struct GateUpArgs {
+  const uint16_t* x;
+  int T, top_k, E, H, I;
+  const int* offsets;
+  const int* sorted_slots;
+  const int* active;
+  const int* num_active;
+  const int* qw;
+  const uint16_t* sc;
+  const int* qz;
+};
+struct DownArgs {
+  int T, top_k, E, H, I;
+  const int* offsets;
+  const int* active;
+  const int* num_active;
+  const int* qw;
+  const uint16_t* sc;
+  const int* qz;
+  float* y;
+};
+void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
+void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
+
+void launch_combine(const float* y_sorted, const float* weights,
+                    const int* slot_rows, int T, int top_k, int H,
+                    uint16_t* out, hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// Device helpers
+// ----------------------------------------------------------------------------
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+// v_dot2_f32_f16: a.lo*b.lo + a.hi*b.hi + c, fp16 products exact in fp32.
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a),
+                                __builtin_bit_cast(h2_t, b), c, false);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+
+// Round to nearest even (the default rounding mode of v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+}  // namespace moe

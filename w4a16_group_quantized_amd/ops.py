@@ -1,0 +1,276 @@
+"""Thin Python binding over libmoe_w4a16.so (C ABI in include/moe_w4a16.h).
+
+Argument marshalling only: each function takes torch tensors, allocates its
+outputs with torch (device memory is the caller's), and passes raw device
+pointers plus torch's current HIP stream to the library.  Every step of the
+layer runs in the library's HIP kernels; there is no fallback, and a missing
+library or a non-OK status raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmoe_w4a16.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+
+GROUP_SIZE = 32
+
+EXPORTED = (
+    "moe_status_string",
+    "moe_abi_version",
+    "moe_route",
+    "moe_permute_workspace_bytes",
+    "moe_permute",
+    "moe_ffn_workspace_bytes",
+    "moe_w4a16_grouped_ffn",
+    "moe_w4a16_gate_up",
+    "moe_w4a16_down",
+    "moe_combine",
+)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
+    "moe_permute_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_ffn_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
+    "moe_w4a16_grouped_ffn": (
+        ctypes.c_int,
+        [_P, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P,
+         _SZ, _P],
+    ),
+    "moe_w4a16_gate_up": (
+        ctypes.c_int,
+        [_P, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _SZ, _P],
+    ),
+    "moe_w4a16_down": (
+        ctypes.c_int,
+        [_I64, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P],
+    ),
+    "moe_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Open the HIP library (once); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m w4a16_group_quantized_amd.build_lib`"
+        )
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(fn, status, status_string(status))
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream() -> int | None:
+    return torch.cuda.current_stream().cuda_stream or None
+
+
+# --------------------------------------------------------------------------- #
+# size queries
+# --------------------------------------------------------------------------- #
+def permute_workspace_bytes(T: int, top_k: int, E: int) -> int:
+    return int(load_library().moe_permute_workspace_bytes(T, top_k, E))
+
+
+def ffn_workspace_bytes(T: int, top_k: int, E: int, H: int, I: int) -> int:
+    return int(load_library().moe_ffn_workspace_bytes(T, top_k, E, H, I))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------- #
+# the four layer calls (plus the two halves of the FFN)
+# --------------------------------------------------------------------------- #
+def moe_route(logits: torch.Tensor, top_k: int, out_ids=None, out_weights=None):
+    """fp32 logits [T, E] -> (topk_ids int32 [T, k], topk_weights fp32 [T, k])."""
+    lib = load_library()
+    T, E = logits.shape
+    dev = logits.device
+    ids = out_ids if out_ids is not None else torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = out_weights if out_weights is not None else torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    _check("moe_route", lib.moe_route(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(w), _stream()))
+    return ids, w
+
+
+def moe_permute(topk_ids: torch.Tensor, E: int, workspace: torch.Tensor | None = None,
+                out: dict | None = None) -> dict:
+    """topk_ids [T, k] -> dict of expert_offsets, sorted_slots, slot_rows, active_experts, num_active."""
+    lib = load_library()
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    S = T * k
+    if out is None:
+        out = {
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "sorted_slots": torch.empty(S, dtype=torch.int32, device=dev),
+            "slot_rows": torch.empty(S, dtype=torch.int32, device=dev),
+            "active_experts": torch.empty(E, dtype=torch.int32, device=dev),
+            "num_active": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+    need = permute_workspace_bytes(T, k, E)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    _check("moe_permute", lib.moe_permute(
+        _ptr(topk_ids), T, k, E, _ptr(out["expert_offsets"]), _ptr(out["sorted_slots"]),
+        _ptr(out["slot_rows"]), _ptr(out["active_experts"]), _ptr(out["num_active"]),
+        _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def _ffn_ws(T, k, E, H, I, workspace, dev):
+    need = ffn_workspace_bytes(T, k, E, H, I)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    return workspace
+
+
+def moe_w4a16_grouped_ffn(x: torch.Tensor, top_k: int, perm: dict, w: dict,
+                          y_sorted: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """x fp16 [T, H] -> y_sorted fp32 [T*k, H] (sorted-row order)."""
+    lib = load_library()
+    T, H = x.shape
+    E = w["w13_q"].shape[0]
+    I = w["w2_q"].shape[2] * 8
+    dev = x.device
+    if y_sorted is None:
+        y_sorted = torch.empty((T * top_k, H), dtype=torch.float32, device=dev)
+    workspace = _ffn_ws(T, top_k, E, H, I, workspace, dev)
+    _check("moe_w4a16_grouped_ffn", lib.moe_w4a16_grouped_ffn(
+        _ptr(x), T, top_k, _ptr(perm["expert_offsets"]), _ptr(perm["sorted_slots"]),
+        _ptr(perm["active_experts"]), _ptr(perm["num_active"]),
+        _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w13_z"]),
+        _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]),
+        E, H, I, GROUP_SIZE, _ptr(y_sorted), _ptr(workspace), workspace.numel(), _stream()))
+    return y_sorted
+
+
+def moe_w4a16_gate_up(x: torch.Tensor, top_k: int, perm: dict, w: dict,
+                      workspace: torch.Tensor) -> None:
+    lib = load_library()
+    T, H = x.shape
+    E = w["w13_q"].shape[0]
+    I = w["w2_q"].shape[2] * 8
+    _check("moe_w4a16_gate_up", lib.moe_w4a16_gate_up(
+        _ptr(x), T, top_k, _ptr(perm["expert_offsets"]), _ptr(perm["sorted_slots"]),
+        _ptr(perm["active_experts"]), _ptr(perm["num_active"]),
+        _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w13_z"]),
+        E, H, I, GROUP_SIZE, _ptr(workspace), workspace.numel(), _stream()))
+
+
+def moe_w4a16_down(T: int, top_k: int, perm: dict, w: dict, y_sorted: torch.Tensor,
+                   workspace: torch.Tensor) -> None:
+    lib = load_library()
+    E, H = w["w2_q"].shape[0], w["w2_q"].shape[1]
+    I = w["w2_q"].shape[2] * 8
+    _check("moe_w4a16_down", lib.moe_w4a16_down(
+        T, top_k, _ptr(perm["expert_offsets"]), _ptr(perm["active_experts"]),
+        _ptr(perm["num_active"]), _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]),
+        E, H, I, GROUP_SIZE, _ptr(y_sorted), _ptr(workspace), workspace.numel(), _stream()))
+
+
+def moe_combine(y_sorted: torch.Tensor, topk_weights: torch.Tensor, slot_rows: torch.Tensor,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """y_sorted fp32 [T*k, H] -> out fp16 [T, H]."""
+    lib = load_library()
+    T, k = topk_weights.shape
+    H = y_sorted.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float16, device=y_sorted.device)
+    _check("moe_combine", lib.moe_combine(
+        _ptr(y_sorted), _ptr(topk_weights), _ptr(slot_rows), T, k, H, _ptr(out), _stream()))
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# one whole layer call
+# --------------------------------------------------------------------------- #
+class MoELayer:
+    """Device-resident buffers for repeated layer calls at one size (graph-capturable)."""
+
+    def __init__(self, T: int, E: int, top_k: int, H: int, I: int, device="cuda"):
+        self.T, self.E, self.top_k, self.H, self.I = T, E, top_k, H, I
+        S = T * top_k
+        dev = torch.device(device)
+        self.ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+        self.weights = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+        self.perm = {
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "sorted_slots": torch.empty(S, dtype=torch.int32, device=dev),
+            "slot_rows": torch.empty(S, dtype=torch.int32, device=dev),
+            "active_experts": torch.empty(E, dtype=torch.int32, device=dev),
+            "num_active": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+        self.perm_ws = _workspace(permute_workspace_bytes(T, top_k, E), dev)
+        self.ffn_ws = _workspace(ffn_workspace_bytes(T, top_k, E, H, I), dev)
+        self.y_sorted = torch.empty((S, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.float16, device=dev)
+
+    def __call__(self, logits: torch.Tensor, x: torch.Tensor, w: dict) -> torch.Tensor:
+        moe_route(logits, self.top_k, self.ids, self.weights)
+        moe_permute(self.ids, self.E, self.perm_ws, self.perm)
+        moe_w4a16_grouped_ffn(x, self.top_k, self.perm, w, self.y_sorted, self.ffn_ws)
+        moe_combine(self.y_sorted, self.weights, self.perm["slot_rows"], self.out)
+        return self.out
+
+
+def weights_to_device(host: dict, device="cuda") -> dict:
+    """numpy weight arrays -> device tensors (int32 and fp16 bit-compatible dtypes)."""
+    out = {}
+    for key in ("w13_q", "w13_z", "w2_q", "w2_z"):
+        out[key] = torch.from_numpy(host[key]).to(device)
+    for key in ("w13_s", "w2_s"):
+        out[key] = torch.from_numpy(host[key]).to(device)
+    return out
