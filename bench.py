@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert W4A16 group-32 MoE layer on one MI355X.
+
+A step is one whole layer call (moe_route, moe_permute, moe_w4a16_grouped_ffn,
+moe_combine) over one batch of seeded synthetic input with every input already
+resident in HBM.  The default workload is the 512-expert, top-10,
+hidden-2560, intermediate-640 layer at 8 decode tokens.
+
+Measurement
+  * The expert weights are cloned into --layers device copies and step s uses
+    copy s % layers, so each step streams its active experts from HBM and not
+    from the 256 MB last-level cache (a model runs its layers one after the
+    other the same way).
+  * value: tokens/s of K steps replayed as HIP graphs (one graph per weight
+    copy), bracketed by device synchronisation.  The same K steps run eagerly
+    first with HIP events around each kernel-bearing call; the dominant
+    kernel's average duration gives the roofline.
+  * cpu_baseline: the CPU oracle (test infrastructure) timed on this host on
+    the same workload, best of a few repeats.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 matrix, AMD published
+DEFAULT_WORKLOAD = "decode_e512_k10_h2560_i640_t8"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=480)
+    p.add_argument("--warmup", type=int, default=48)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--layers", type=int, default=16, help="device copies of the expert weights")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-graph", action="store_true", help="report the eager loop as value")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-repeats", type=int, default=3)
+    return p.parse_args(argv)
+
+
+# --------------------------------------------------------------------------- #
+# algorithmic work (what the layer must move / compute)
+# --------------------------------------------------------------------------- #
+def expert_bytes(H: int, I: int) -> tuple[int, int]:
+    """Bytes of one expert's w13 and w2: int4 codes + fp16 scales + packed zeros."""
+    def mat(N, K):
+        return N * K // 2 + N * (K // 32) * 2 + (N // 8) * (K // 32) * 4
+    return mat(2 * I, H), mat(H, I)
+
+
+def layer_work(shape, num_active: int) -> dict:
+    w13, w2 = expert_bytes(shape.H, shape.I)
+    io = shape.T * shape.H * 2 + shape.T * shape.E * 4 + shape.T * shape.H * 2
+    return {
+        "w13_bytes_per_expert": w13,
+        "w2_bytes_per_expert": w2,
+        "layer_bytes": num_active * (w13 + w2) + io,
+        "gate_up_bytes": num_active * w13 + shape.T * shape.H * 2,
+        "down_bytes": num_active * w2,
+        "flops": 6 * shape.T * shape.top_k * shape.H * shape.I,
+        "gate_up_flops": 4 * shape.T * shape.top_k * shape.H * shape.I,
+    }
+
+
+# --------------------------------------------------------------------------- #
+# CPU baseline: the oracle on this host
+# --------------------------------------------------------------------------- #
+def cpu_baseline(host: dict, shape, repeats: int) -> dict:
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max(blas) if blas else 1
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    sample_T = shape.T
+    sub = host
+    if shape.T > 64:  # bounded sample of the same workload: its first 64 tokens
+        sample_T = 64
+        sub = dict(host)
+        sub["logits"] = host["logits"][:64]
+        sub["x"] = host["x"][:64]
+    best = float("inf")
+    for _ in range(max(1, repeats)):
+        t0 = time.perf_counter()
+        oracle.layer(sub, shape.top_k)
+        best = min(best, time.perf_counter() - t0)
+    _ = np
+    return {
+        "value": sample_T / best,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"whole layer on the first {sample_T} tokens of the workload, best of {repeats}, "
+                  f"fp64 NumPy (unpack single-threaded, BLAS on {threads} threads), "
+                  f"{len(os.sched_getaffinity(0))} host cores visible",
+        "seconds": best,
+    }
+
+
+# --------------------------------------------------------------------------- #
+# GPU measurement
+# --------------------------------------------------------------------------- #
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the MoE layer on a single MI355X "
+              "and has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from w4a16_group_quantized_amd import inputs as synth
+    from w4a16_group_quantized_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    shape = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.load_library()
+    log(f"workload {args.workload}: {shape} on {torch.cuda.get_device_name(dev)}")
+
+    host = synth.make_inputs(shape, args.seed)
+    logits = torch.from_numpy(host["logits"]).to(dev)
+    x = torch.from_numpy(host["x"]).to(dev)
+    w0 = ops.weights_to_device(host, dev)
+    copies = [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(args.layers - 1)]
+    per_copy = sum(v.numel() * v.element_size() for v in w0.values())
+    log(f"{args.layers} weight copies x {per_copy / 2**30:.2f} GiB on device")
+
+    layer = ops.MoELayer(shape.T, shape.E, shape.top_k, shape.H, shape.I, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i: int, ev=None):
+        w = copies[i % args.layers]
+        if ev is not None:
+            ev[0].record(stream)
+        ops.moe_route(logits, shape.top_k, layer.ids, layer.weights)
+        ops.moe_permute(layer.ids, shape.E, layer.perm_ws, layer.perm)
+        if ev is not None:
+            ev[1].record(stream)
+        ops.moe_w4a16_gate_up(x, shape.top_k, layer.perm, w, layer.ffn_ws)
+        if ev is not None:
+            ev[2].record(stream)
+        ops.moe_w4a16_down(shape.T, shape.top_k, layer.perm, w, layer.y_sorted, layer.ffn_ws)
+        if ev is not None:
+            ev[3].record(stream)
+        ops.moe_combine(layer.y_sorted, layer.weights, layer.perm["slot_rows"], layer.out)
+        if ev is not None:
+            ev[4].record(stream)
+
+    # warm-up (eager), then the eager timed pass with per-call events
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ref_out = layer.out.clone()
+    num_active = int(layer.perm["num_active"].item())
+    work = layer_work(shape, num_active)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = t_start.elapsed_time(t_end) / args.steps
+    seg = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
+    seg_ms = seg.mean(axis=0)
+    log(f"eager: {eager_ms * 1e3:.1f} us/step; route+permute {seg_ms[0] * 1e3:.1f}, "
+        f"gate_up {seg_ms[1] * 1e3:.1f}, down {seg_ms[2] * 1e3:.1f}, combine {seg_ms[3] * 1e3:.1f} us")
+    assert torch.equal(layer.out, ref_out), "eager steps disagree"
+
+    # HIP graphs: one captured step per weight copy, replayed round-robin
+    graph_ms = None
+    if not args.no_graph:
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for c in range(args.layers):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    step(c)
+                graphs.append(g)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        for rep in range(3):  # every replay must reproduce the eager result
+            layer.out.zero_()
+            graphs[rep % args.layers].replay()
+            torch.cuda.synchronize()
+            assert torch.equal(layer.out, ref_out), "graph replay differs from eager"
+        for i in range(args.warmup):
+            graphs[i % args.layers].replay()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(args.steps):
+            graphs[i % args.layers].replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = t_start.elapsed_time(t_end) / args.steps
+        assert torch.equal(layer.out, ref_out), "graph replay differs from eager"
+        log(f"graph: {graph_ms * 1e3:.1f} us/step")
+
+    ms = graph_ms if graph_ms is not None else eager_ms
+    tokens_per_s = shape.T / (ms * 1e-3)
+    gate_up_s = seg_ms[1] * 1e-3
+    achieved = work["gate_up_bytes"] / gate_up_s / 1e9
+    result = {
+        "metric": "MoE layer tokens/s (decode: HBM GB/s of the gate/up kernel in roofline)",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "w4a16 (int4 weights, fp16 activations, fp32 accumulation)",
+        "data": "synthetic (seeded; weights random uint4 codes/zeros, fp16 scales U[0.002,0.02))",
+        "config": {
+            "workload": args.workload,
+            "E": shape.E, "top_k": shape.top_k, "H": shape.H, "I": shape.I, "T": shape.T,
+            "group_size": 32, "weight_copies": args.layers, "active_experts": num_active,
+            "timing": "hip-graph replay" if graph_ms is not None else "eager",
+        },
+        "roofline": {
+            "kernel": "gate_up_decode_kernel (moe_w4a16_gate_up)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "avg_launch_us": seg_ms[1] * 1e3,
+            "algorithmic_bytes_per_launch": work["gate_up_bytes"],
+        },
+        "layer": {
+            "eager_us_per_step": eager_ms * 1e3,
+            "graph_us_per_step": graph_ms * 1e3 if graph_ms is not None else None,
+            "algorithmic_bytes": work["layer_bytes"],
+            "layer_GBps": work["layer_bytes"] / (ms * 1e-3) / 1e9,
+            "layer_hbm_frac": work["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "flops": work["flops"],
+            "TFLOPs": work["flops"] / (ms * 1e-3) / 1e12,
+            "mfma_frac": work["flops"] / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "segments_us": {"route+permute": seg_ms[0] * 1e3, "gate_up": seg_ms[1] * 1e3,
+                            "down": seg_ms[2] * 1e3, "combine": seg_ms[3] * 1e3},
+            "down_GBps": work["down_bytes"] / (seg_ms[2] * 1e-3) / 1e9,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(host, shape, args.cpu_repeats)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -231,3 +231,34 @@ def test_gate_up_then_down_equals_grouped_ffn(dev):
     ops.moe_w4a16_down(shape.T, shape.top_k, perm, w, y_b, ws)
     torch.cuda.synchronize()
     assert torch.equal(y_a, y_b)
+
+
+@pytest.mark.parametrize("T", [8, 300])
+def test_graph_replay_matches_eager(dev, T):
+    """A captured layer call replays to the eager result, with eager work between replays."""
+    from w4a16_group_quantized_amd import ops
+
+    shape = synth.MoEShape(E=64, top_k=6, H=512, I=256, T=T)
+    host = synth.make_inputs(shape, 21)
+    w = ops.weights_to_device(host, dev)
+    logits = torch.from_numpy(host["logits"]).to(dev)
+    x = torch.from_numpy(host["x"]).to(dev)
+    layer = ops.MoELayer(shape.T, shape.E, shape.top_k, shape.H, shape.I, dev)
+    eager = layer(logits, x, w).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            layer(logits, x, w)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        layer.out.fill_(7.0)
+        layer.y_sorted.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.out, eager), f"replay {rep}"
+        _ = (layer.out.float() * 2).sum().item()  # eager work between replays

@@ -6,15 +6,18 @@
 // over active experts of "[Perf][SM70] Narrow Qwen3.8 AWQ active grouped
 // decode", section "Purpose"; group size 32 along K).
 //
-// Work split.  A workgroup takes one active expert and one tile of weight rows
-// (stage 1: NT gate rows with the matching NT up rows, so SiLU(gate)*up is
-// formed in the epilogue).  Its G * P threads form a G x P grid: thread
-// (g, p) owns quantisation group g (32 consecutive k, one 16-byte load per
-// weight row) and the tile rows p, p + P, ...  The weight words, fp16 scale
-// and 4-bit zero of its rows are loaded once into registers, so each weight
-// byte is read from HBM exactly once; the expert's rows of A (x rows gathered
-// through the sorted slots, or the act rows) are processed in chunks of up to
-// two, each chunk's 32-value slice of A sitting in registers.
+// Work split.  A cluster of C lanes owns one weight row; lane c of the
+// cluster takes the row's quantisation groups c, c + C, ... (one 16-byte load
+// of codes per group), so each step of a wave reads C * 16 contiguous bytes
+// from each of its 64 / C rows.  A wave owns a contiguous run of row blocks of
+// one expert (stage 1: a block is R/2 gate rows in the lower half of the wave
+// and the matching R/2 up rows in the upper half, R = 64 / C), steps through
+// them with a ring of kDepth register slots of weight loads in flight, and
+// sums a row's groups within the cluster with DPP once the row is done;
+// nothing is synchronised across waves in the streaming loop.  The expert's
+// rows of A (x rows gathered through the sorted slots, or act rows) are staged
+// once per workgroup in LDS, already paired to the nibble layout, and read
+// back as broadcasts.  The grid is sized to what the chip holds at once.
 //
 // Arithmetic.  A nibble q is turned into the fp16 number 1024 + q by OR-ing
 // it into the mantissa of 0x6400 (nibbles in bits 4..7 of a half give
@@ -23,8 +26,8 @@
 // the zero point are removed once per group:
 //   sum_k (q_k - z) a_k = accA + accB / 16 - (1024 S_lo + 64 S_hi) - z S,
 // with S_lo, S_hi the sums of A over the two nibble position classes and
-// S = S_lo + S_hi; the group's fp16 scale is applied in fp32.  Partial sums of
-// the G groups are combined in a fixed order through LDS.
+// S = S_lo + S_hi; the group's fp16 scale is applied in fp32.  The order of
+// every sum is fixed, so results do not depend on scheduling.
 //
 // Precision of the down product.  act is stored as act_hi = fp16(act) and
 // act_lo = fp16(act - act_hi) and both halves are multiplied, which carries
@@ -36,351 +39,391 @@
 namespace moe {
 namespace {
 
-constexpr uint32_t kBias = 0x64006400u;  // fp16 1024.0 in both halves
-constexpr uint32_t kOnes = 0x3C003C00u;  // fp16 1.0 in both halves
-constexpr int kMaxThreads = 512;
+constexpr uint32_t kOnes = 0x3C003C00u;   // fp16 1.0 in both halves
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDepth = 8;                 // weight loads in flight per lane (ring slots)
+constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for raw dword access on gfx9
+constexpr int kFragDwords = 20;           // LDS dwords per (A row, group): 16 pairs, c1, s, pad
 
-// One A row's 32 values of this thread's group, paired to match the nibble
-// positions: for 8-value block w, pairs (a0,a4), (a1,a5), (a2,a6), (a3,a7).
-struct AFrag {
-  uint32_t p[4][4];
-  float c1;  // 1024 * S_lo + 64 * S_hi
-  float s;   // S_lo + S_hi
-};
-
-__device__ __forceinline__ void load_afrag(const uint16_t* __restrict__ src, AFrag& f) {
+// ------------------------------------------------------------ A fragments ---
+// One A row's 32 values of a group, paired to match the nibble positions: for
+// 8-value block w, pairs (a0,a4), (a1,a5), (a2,a6), (a3,a7); plus
+// c1 = 1024 S_lo + 64 S_hi and s = S_lo + S_hi.  Written to LDS once.
+__device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ src, uint32_t* dst) {
   const uint4* q = reinterpret_cast<const uint4*>(src);
+  uint32_t p[16];
   float slo = 0.f, shi = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint4 d = q[w];  // d.x = (a0,a1), d.y = (a2,a3), d.z = (a4,a5), d.w = (a6,a7)
-    f.p[w][0] = (d.x & 0xFFFFu) | (d.z << 16);
-    f.p[w][1] = (d.x >> 16) | (d.z & 0xFFFF0000u);
-    f.p[w][2] = (d.y & 0xFFFFu) | (d.w << 16);
-    f.p[w][3] = (d.y >> 16) | (d.w & 0xFFFF0000u);
-    slo = dot2_f16(f.p[w][0], kOnes, slo);
-    slo = dot2_f16(f.p[w][2], kOnes, slo);
-    shi = dot2_f16(f.p[w][1], kOnes, shi);
-    shi = dot2_f16(f.p[w][3], kOnes, shi);
+    p[4 * w + 0] = (d.x & 0xFFFFu) | (d.z << 16);
+    p[4 * w + 1] = (d.x >> 16) | (d.z & 0xFFFF0000u);
+    p[4 * w + 2] = (d.y & 0xFFFFu) | (d.w << 16);
+    p[4 * w + 3] = (d.y >> 16) | (d.w & 0xFFFF0000u);
+    slo = dot2_f16(p[4 * w + 0], kOnes, slo);
+    slo = dot2_f16(p[4 * w + 2], kOnes, slo);
+    shi = dot2_f16(p[4 * w + 1], kOnes, shi);
+    shi = dot2_f16(p[4 * w + 3], kOnes, shi);
   }
-  f.c1 = 1024.f * slo + 64.f * shi;
-  f.s = slo + shi;
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d4[i] = make_uint4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+  *reinterpret_cast<uint2*>(dst + 16) =
+      make_uint2(__builtin_bit_cast(uint32_t, 1024.f * slo + 64.f * shi),
+                 __builtin_bit_cast(uint32_t, slo + shi));
 }
 
-// sum_k (q_k - z) a_k over one group for NA rows of A.
-template <int NA>
-__device__ __forceinline__ void group_dot(const uint4 qv, float z, const AFrag (&a)[NA],
-                                          float (&res)[NA]) {
-  float ta[NA], tb[NA];
-#pragma unroll
-  for (int m = 0; m < NA; ++m) {
-    ta[m] = 0.f;
-    tb[m] = 0.f;
-  }
+// Nibble codes of one group as biased fp16 pairs (see the file comment).
+struct Codes {
+  uint32_t a[4], b[4], c[4], d[4];
+};
+
+__device__ __forceinline__ Codes expand_codes(const uint4 qv) {
+  // The bias lives in a vector register: gfx9 VOP3 takes no literal and one
+  // scalar operand, so with the mask in a scalar register each mask-and-insert
+  // is a single v_and_or_b32.
+  uint32_t bias;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));
   const uint32_t words[4] = {qv.x, qv.y, qv.z, qv.w};
+  Codes k;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint32_t v = words[w];
     const uint32_t v8 = v >> 8;
-    const uint32_t pa = (v & 0x000F000Fu) | kBias;   // 1024 + q0, 1024 + q4
-    const uint32_t pb = (v & 0x00F000F0u) | kBias;   // 1024 + 16 q1, 1024 + 16 q5
-    const uint32_t pc = (v8 & 0x000F000Fu) | kBias;  // 1024 + q2, 1024 + q6
-    const uint32_t pd = (v8 & 0x00F000F0u) | kBias;  // 1024 + 16 q3, 1024 + 16 q7
-#pragma unroll
-    for (int m = 0; m < NA; ++m) {
-      ta[m] = dot2_f16(pa, a[m].p[w][0], ta[m]);
-      tb[m] = dot2_f16(pb, a[m].p[w][1], tb[m]);
-      ta[m] = dot2_f16(pc, a[m].p[w][2], ta[m]);
-      tb[m] = dot2_f16(pd, a[m].p[w][3], tb[m]);
-    }
+    k.a[w] = (v & 0x000F000Fu) | bias;   // 1024 + q0, 1024 + q4
+    k.b[w] = (v & 0x00F000F0u) | bias;   // 1024 + 16 q1, 1024 + 16 q5
+    k.c[w] = (v8 & 0x000F000Fu) | bias;  // 1024 + q2, 1024 + q6
+    k.d[w] = (v8 & 0x00F000F0u) | bias;  // 1024 + 16 q3, 1024 + 16 q7
   }
-#pragma unroll
-  for (int m = 0; m < NA; ++m) res[m] = fmaf(-z, a[m].s, fmaf(tb[m], 0.0625f, ta[m]) - a[m].c1);
+  return k;
 }
 
-// Register-resident quantised rows of one thread.
-template <int RT>
-struct WRows {
-  uint4 q[RT];
-  float s[RT];
-  float z[RT];
+// sum_k (q_k - z) a_k over one group, A fragment read from LDS.
+__device__ __forceinline__ float group_dot(const Codes& k, float z, const uint32_t* frag) {
+  const uint4* f4 = reinterpret_cast<const uint4*>(frag);
+  float ta = 0.f, tb = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint4 f = f4[w];
+    ta = dot2_f16(k.a[w], f.x, ta);
+    tb = dot2_f16(k.b[w], f.y, tb);
+    ta = dot2_f16(k.c[w], f.z, ta);
+    tb = dot2_f16(k.d[w], f.w, tb);
+  }
+  const uint2 cs = *reinterpret_cast<const uint2*>(frag + 16);
+  return fmaf(-z, __builtin_bit_cast(float, cs.y),
+              fmaf(tb, 0.0625f, ta) - __builtin_bit_cast(float, cs.x));
+}
+
+// ------------------------------------------------------------ weight ring ---
+// One step's loads, kept exactly as loaded until the step is computed.
+struct Slot {
+  uint4 q;
+  uint32_t s;
+  uint32_t zw;
 };
 
-template <int RT>
-__device__ __forceinline__ void load_wrows(const int* __restrict__ qw, const uint16_t* __restrict__ sc,
-                                           const int* __restrict__ qz, int G, int g,
-                                           const int (&n)[RT], const bool (&valid)[RT],
-                                           WRows<RT>& w) {
-  const int KW = G * 4;  // int32 words per row
+struct ExpertBufs {
+  __amdgpu_buffer_rsrc_t q, s, z;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           kBufferFlags);
+}
+
+// Raw buffer loads take a 32-bit offset against a uniform base and return 0
+// past the end without touching memory, so a row index of `rows` is a free
+// "no load".
+__device__ __forceinline__ ExpertBufs expert_bufs(const int* qw, const uint16_t* sc, const int* qz,
+                                                  int rows, int G) {
+  ExpertBufs b;
+  b.q = make_rsrc(qw, static_cast<uint32_t>(rows) * G * 16u);
+  b.s = make_rsrc(sc, static_cast<uint32_t>(rows) * G * 2u);
+  b.z = make_rsrc(qz, static_cast<uint32_t>(rows / 8) * G * 4u);
+  return b;
+}
+
+__device__ __forceinline__ void load_slot(const ExpertBufs& b, int G, uint32_t row, uint32_t g,
+                                          Slot& s) {
+  const uint32_t idx = __umul24(row, G) + g;
+  const auto qv = __builtin_amdgcn_raw_buffer_load_b128(b.q, static_cast<int>(idx * 16u), 0, 0);
+  s.q = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+  s.s = __builtin_amdgcn_raw_buffer_load_b16(b.s, static_cast<int>(idx * 2u), 0, 0);
+  s.zw = __builtin_amdgcn_raw_buffer_load_b32(
+      b.z, static_cast<int>((__umul24(row >> 3, G) + g) * 4u), 0, 0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+  return v + __builtin_bit_cast(float, moved);
+}
+
+// Sum over each aligned cluster of C lanes (C a power of two <= 16); every
+// lane of the cluster gets the sum.  Called with all lanes of the wave active.
+__device__ __forceinline__ float cluster_sum(float v, int C) {
+  if (C >= 2) v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]: partner lane ^ 1
+  if (C >= 4) v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]: partner lane ^ 2
+  if (C >= 8) v = dpp_add<0x141>(v);  // row_half_mirror: lane i <-> 7 - i within 8
+  if (C >= 16) v = dpp_add<0x140>(v); // row_mirror: lane i <-> 15 - i within 16
+  return v;
+}
+
+// Geometry of one stage, fixed per launch.
+struct Geom {
+  int G;       // groups along K
+  int C;       // lanes per row (cluster); rows per wave block R = 64 / C
+  int spb;     // steps per block = ceil(G / C)
+  int nb;      // blocks per expert
+  int bpw;     // blocks per wave
+  int splits;  // workgroups per active-expert slot
+};
+
+// Weight row that lane cluster k reads in block b, or `rows` when there is
+// none.  Stage 1: lower half of the wave gate rows, upper half up rows.
+template <bool GATE_UP>
+__device__ __forceinline__ int block_row(int b, int k, int R, int I, int H) {
+  if (GATE_UP) {
+    const int half = R >> 1;
+    const int col = b * half + (k < half ? k : k - half);
+    if (col >= I) return 2 * I;
+    return k < half ? col : I + col;
+  }
+  const int n = b * R + k;
+  return n < H ? n : H;
+}
+
+// ------------------------------------------------------------------ kernel --
+// Streams blocks [b0, b1) of one expert for mc (<= NA) rows of A.  Stage 2
+// fragments come in (hi, lo) pairs: fragment 2m is act_hi of row m, 2m + 1
+// its act_lo.
+template <bool GATE_UP, int NA>
+__device__ __forceinline__ void stream_expert(const ExpertBufs& bufs, const Geom& geo, int rows_w,
+                                              int I, int H, int b0, int b1, const uint32_t* frags,
+                                              int mc, int r_first, uint16_t* act_hi,
+                                              uint16_t* act_lo, float* y) {
+  const int lane = threadIdx.x & 63;
+  const int C = geo.C;
+  const int R = 64 / C;
+  const int k = lane / C;
+  const int lc = lane & (C - 1);
+  const int G = geo.G;
+  const int spb = geo.spb;
+  const int S = (b1 - b0) * spb;
+
+  Slot ring[kDepth];
 #pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    if (valid[i]) {
-      w.q[i] = *reinterpret_cast<const uint4*>(qw + static_cast<size_t>(n[i]) * KW + 4 * g);
-      w.s[i] = half_bits_to_float(sc[static_cast<size_t>(n[i]) * G + g]);
-      const uint32_t zw = static_cast<uint32_t>(qz[static_cast<size_t>(n[i] >> 3) * G + g]);
-      w.z[i] = static_cast<float>((zw >> (4 * (n[i] & 7))) & 0xFu);
-    } else {
-      w.q[i] = make_uint4(0u, 0u, 0u, 0u);
-      w.s[i] = 0.f;
-      w.z[i] = 0.f;
+  for (int d = 0; d < kDepth; ++d) {
+    const int gg = (d % spb) * C + lc;
+    const bool live = d < S && gg < G;
+    const uint32_t row = live ? block_row<GATE_UP>(b0 + d / spb, k, R, I, H) : rows_w;
+    load_slot(bufs, G, row, live ? gg : 0, ring[d]);
+  }
+
+  constexpr int NF = GATE_UP ? NA : 2 * NA;  // fragments per chunk of A rows
+  const int nf = GATE_UP ? mc : 2 * mc;
+  float acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = 0.f;
+
+  for (int s0 = 0; s0 < S; s0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int s = s0 + d;
+      if (s < S) {
+        const int b = b0 + s / spb;
+        const int j = s - (s / spb) * spb;
+        const int gg = j * C + lc;
+        const uint32_t row = static_cast<uint32_t>(block_row<GATE_UP>(b, k, R, I, H));
+        const Slot& sl = ring[d];
+        const float scale = half_bits_to_float(static_cast<uint16_t>(sl.s));
+        const float z = static_cast<float>((sl.zw >> (4u * (row & 7u))) & 0xFu);
+        const Codes codes = expand_codes(sl.q);
+        const uint32_t* fr = frags + (gg < G ? gg : 0) * kFragDwords;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          if (f < nf) acc[f] = fmaf(scale, group_dot(codes, z, fr + f * G * kFragDwords), acc[f]);
+        if (j == spb - 1) {  // block done: finish its rows
+#pragma unroll
+          for (int m = 0; m < NA; ++m) {
+            if (m < mc) {
+              if (GATE_UP) {
+                const float v = cluster_sum(acc[m], C);
+                const float u = __shfl_xor(v, 32, 64);  // up half of the wave -> gate half
+                const int col = b * (R >> 1) + k;
+                if (lane < 32 && lc == 0 && col < I) {
+                  const float act = v / (1.f + expf(-v)) * u;
+                  const uint16_t hi = float_to_half_bits(act);
+                  const uint16_t lo = float_to_half_bits(act - half_bits_to_float(hi));
+                  const size_t idx = static_cast<size_t>(r_first + m) * I + col;
+                  act_hi[idx] = hi;
+                  act_lo[idx] = lo;
+                }
+              } else {
+                const float v = cluster_sum(acc[2 * m] + acc[2 * m + 1], C);
+                const int n = b * R + k;
+                if (lc == 0 && n < H) y[static_cast<size_t>(r_first + m) * H + n] = v;
+              }
+            }
+          }
+#pragma unroll
+          for (int f = 0; f < NF; ++f) acc[f] = 0.f;
+        }
+      }
+      // Refill this slot with the step kDepth ahead; past the end this is a
+      // no-load, issued anyway so every path keeps the same wait counts.
+      const int sn = s + kDepth;
+      const int gn = (sn % spb) * C + lc;
+      const bool live = sn < S && gn < G;
+      const uint32_t rown = live ? block_row<GATE_UP>(b0 + sn / spb, k, R, I, H) : rows_w;
+      load_slot(bufs, G, rown, live ? gn : 0, ring[d]);
     }
   }
 }
 
-// Sum red[(lr * SL + m) * G + 0..G-1] into sum[lr * SL + m] for lr < rows, m < na.
-template <int SL>
-__device__ __forceinline__ void reduce_groups(const float* red, float* sum, int rows, int na, int G) {
-  for (int o = threadIdx.x; o < rows * na; o += blockDim.x) {
-    const int lr = o / na;
-    const int m = o - lr * na;
-    const float* src = red + (lr * SL + m) * G;
-    float acc = 0.f;
-    for (int gg = 0; gg < G; ++gg) acc += src[gg];
-    sum[lr * SL + m] = acc;
-  }
-}
-
-// ---------------------------------------------------------------- stage 1 ---
-template <int NA, int RT, int SL>
-__device__ __forceinline__ void gate_up_chunk(const GateUpArgs& args, const FfnWorkspace& ws,
-                                              const WRows<RT>& w, int G, int P, int NT,
-                                              int tile, int r0, int m0, float* red, float* sum) {
-  const int g = threadIdx.x % G;
-  const int p = threadIdx.x / G;
-  AFrag a[NA];
-#pragma unroll
-  for (int m = 0; m < NA; ++m) {
-    const int token = args.sorted_slots[r0 + m0 + m] / args.top_k;
-    load_afrag(args.x + static_cast<size_t>(token) * args.H + 32 * g, a[m]);
-  }
-#pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    float d[NA];
-    group_dot<NA>(w.q[i], w.z[i], a, d);
-    const int lr = p + P * i;
-#pragma unroll
-    for (int m = 0; m < NA; ++m) red[(lr * SL + m) * G + g] = w.s[i] * d[m];
-  }
-  __syncthreads();
-  reduce_groups<SL>(red, sum, P * RT, NA, G);
-  __syncthreads();
-  for (int o = threadIdx.x; o < NT * NA; o += blockDim.x) {
-    const int c = o / NA;
-    const int m = o - c * NA;
-    const int col = tile * NT + c;
-    if (col < args.I) {
-      const float gate = sum[c * SL + m];
-      const float up = sum[(NT + c) * SL + m];
-      const float act = gate / (1.f + expf(-gate)) * up;
-      const uint16_t hi = float_to_half_bits(act);
-      const uint16_t lo = float_to_half_bits(act - half_bits_to_float(hi));
-      const size_t idx = static_cast<size_t>(r0 + m0 + m) * args.I + col;
-      ws.act_hi[idx] = hi;
-      ws.act_lo[idx] = lo;
-    }
-  }
-  __syncthreads();  // red / sum are reused by the next chunk
-}
-
-template <int RT, int NAMAX>
-__global__ __launch_bounds__(kMaxThreads) void gate_up_decode_kernel(GateUpArgs args,
-                                                                     FfnWorkspace ws, int G,
-                                                                     int P, int NT,
-                                                                     int n_tiles) {
-  extern __shared__ float lds[];
-  const int a_idx = blockIdx.x / n_tiles;
-  const int tile = blockIdx.x - a_idx * n_tiles;
-  if (a_idx >= *args.num_active) return;
-  const int e = args.active[a_idx];
-  const int r0 = args.offsets[e];
-  const int rows_e = args.offsets[e + 1] - r0;
-  const int I = args.I;
-  const int g = threadIdx.x % G;
-  const int p = threadIdx.x / G;
-
-  int n[RT];
-  bool valid[RT];
-#pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    const int lr = p + P * i;
-    const int c = (lr < NT) ? lr : lr - NT;
-    const int col = tile * NT + c;
-    valid[i] = col < I;
-    n[i] = (lr < NT) ? col : I + col;
-  }
+template <int NA>
+__global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(GateUpArgs args, FfnWorkspace ws,
+                                                                  Geom geo) {
+  extern __shared__ uint32_t frags[];
+  const int a_idx = blockIdx.x / geo.splits;
+  const int split = blockIdx.x - a_idx * geo.splits;
+  const int n_active = *args.num_active;
+  const int e = args.active[a_idx];  // in bounds: a_idx < min(E, T * top_k)
+  if (a_idx >= n_active) return;
+  const int I = args.I, H = args.H, G = geo.G;
+  const int wave_id = split * kWaves + (threadIdx.x >> 6);
+  const int b0 = min(geo.nb, wave_id * geo.bpw);
+  const int b1 = min(geo.nb, b0 + geo.bpw);
   const size_t rows_w = static_cast<size_t>(2 * I);
-  WRows<RT> w;
-  load_wrows<RT>(args.qw + static_cast<size_t>(e) * rows_w * (G * 4),
-                 args.sc + static_cast<size_t>(e) * rows_w * G,
-                 args.qz + static_cast<size_t>(e) * (rows_w / 8) * G, G, g, n, valid, w);
-
-  float* red = lds;
-  float* sum = lds + P * RT * NAMAX * G;
-  for (int m0 = 0; m0 < rows_e; m0 += NAMAX) {
-    if (NAMAX == 1 || rows_e - m0 == 1)
-      gate_up_chunk<1, RT, NAMAX>(args, ws, w, G, P, NT, tile, r0, m0, red, sum);
-    else
-      gate_up_chunk<(NAMAX > 1 ? 2 : 1), RT, NAMAX>(args, ws, w, G, P, NT, tile, r0, m0, red, sum);
-  }
-}
-
-// ---------------------------------------------------------------- stage 2 ---
-template <int MR, int RT, int SL>
-__device__ __forceinline__ void down_chunk(const DownArgs& args, const FfnWorkspace& ws,
-                                           const WRows<RT>& w, int G, int P, int tile, int r0,
-                                           int m0, float* red, float* sum) {
-  const int g = threadIdx.x % G;
-  const int p = threadIdx.x / G;
-  AFrag a[2 * MR];  // [hi rows..., lo rows...]
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    const size_t off = static_cast<size_t>(r0 + m0 + m) * args.I + 32 * g;
-    load_afrag(ws.act_hi + off, a[m]);
-    load_afrag(ws.act_lo + off, a[MR + m]);
-  }
-#pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    float d[2 * MR];
-    group_dot<2 * MR>(w.q[i], w.z[i], a, d);
-    const int lr = p + P * i;
-#pragma unroll
-    for (int m = 0; m < MR; ++m) red[(lr * SL + m) * G + g] = w.s[i] * (d[m] + d[MR + m]);
-  }
-  __syncthreads();
-  reduce_groups<SL>(red, sum, P * RT, MR, G);
-  __syncthreads();
-  const int rows = P * RT;
-  for (int o = threadIdx.x; o < rows * MR; o += blockDim.x) {
-    const int m = o / rows;
-    const int lr = o - m * rows;
-    const int nrow = tile * rows + lr;
-    if (nrow < args.H) args.y[static_cast<size_t>(r0 + m0 + m) * args.H + nrow] = sum[lr * SL + m];
-  }
-  __syncthreads();
-}
-
-template <int RT, int MRMAX>
-__global__ __launch_bounds__(kMaxThreads) void down_decode_kernel(DownArgs args, FfnWorkspace ws,
-                                                                  int G, int P, int n_tiles) {
-  extern __shared__ float lds[];
-  const int a_idx = blockIdx.x / n_tiles;
-  const int tile = blockIdx.x - a_idx * n_tiles;
-  if (a_idx >= *args.num_active) return;
-  const int e = args.active[a_idx];
+  const ExpertBufs bufs = expert_bufs(args.qw + static_cast<size_t>(e) * rows_w * (G * 4),
+                                      args.sc + static_cast<size_t>(e) * rows_w * G,
+                                      args.qz + static_cast<size_t>(e) * (rows_w / 8) * G,
+                                      2 * I, G);
   const int r0 = args.offsets[e];
   const int rows_e = args.offsets[e + 1] - r0;
-  const int g = threadIdx.x % G;
-  const int p = threadIdx.x / G;
-  const int rows = P * RT;
-
-  int n[RT];
-  bool valid[RT];
-#pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    n[i] = tile * rows + p + P * i;
-    valid[i] = n[i] < args.H;
-  }
-  const size_t H = static_cast<size_t>(args.H);
-  WRows<RT> w;
-  load_wrows<RT>(args.qw + static_cast<size_t>(e) * H * (G * 4),
-                 args.sc + static_cast<size_t>(e) * H * G,
-                 args.qz + static_cast<size_t>(e) * (H / 8) * G, G, g, n, valid, w);
-
-  float* red = lds;
-  float* sum = lds + rows * MRMAX * G;
-  for (int m0 = 0; m0 < rows_e; m0 += MRMAX) {
-    if (MRMAX == 1 || rows_e - m0 == 1)
-      down_chunk<1, RT, MRMAX>(args, ws, w, G, P, tile, r0, m0, red, sum);
-    else
-      down_chunk<(MRMAX > 1 ? 2 : 1), RT, MRMAX>(args, ws, w, G, P, tile, r0, m0, red, sum);
+  for (int m0 = 0; m0 < rows_e; m0 += NA) {
+    const int mc = min(NA, rows_e - m0);
+    if (m0 > 0) __syncthreads();  // previous chunk's fragments are no longer read
+    for (int i = threadIdx.x; i < mc * G; i += kThreads) {
+      const int m = i / G;
+      const int g = i - m * G;
+      const int token = args.sorted_slots[r0 + m0 + m] / args.top_k;
+      stage_frag(args.x + static_cast<size_t>(token) * H + 32 * g, frags + i * kFragDwords);
+    }
+    __syncthreads();
+    stream_expert<true, NA>(bufs, geo, 2 * I, I, H, b0, b1, frags, mc, r0 + m0, ws.act_hi,
+                            ws.act_lo, nullptr);
   }
 }
 
-// Largest power of two P with G * P <= kMaxThreads.
-int row_phases(int G) {
-  int P = 1;
-  while (G * P * 2 <= kMaxThreads) P *= 2;
-  return P;
+template <int NA>
+__global__ __launch_bounds__(kThreads) void down_decode_kernel(DownArgs args, FfnWorkspace ws,
+                                                               Geom geo) {
+  extern __shared__ uint32_t frags[];
+  const int a_idx = blockIdx.x / geo.splits;
+  const int split = blockIdx.x - a_idx * geo.splits;
+  const int n_active = *args.num_active;
+  const int e = args.active[a_idx];
+  if (a_idx >= n_active) return;
+  const int I = args.I, H = args.H, G = geo.G;
+  const int wave_id = split * kWaves + (threadIdx.x >> 6);
+  const int b0 = min(geo.nb, wave_id * geo.bpw);
+  const int b1 = min(geo.nb, b0 + geo.bpw);
+  const size_t rows_w = static_cast<size_t>(H);
+  const ExpertBufs bufs = expert_bufs(args.qw + static_cast<size_t>(e) * rows_w * (G * 4),
+                                      args.sc + static_cast<size_t>(e) * rows_w * G,
+                                      args.qz + static_cast<size_t>(e) * (rows_w / 8) * G, H, G);
+  const int r0 = args.offsets[e];
+  const int rows_e = args.offsets[e + 1] - r0;
+  for (int m0 = 0; m0 < rows_e; m0 += NA) {
+    const int mc = min(NA, rows_e - m0);
+    if (m0 > 0) __syncthreads();
+    // fragment f = 2 m + {0: hi, 1: lo} of act row r0 + m0 + m, at f * G + g
+    for (int i = threadIdx.x; i < 2 * mc * G; i += kThreads) {
+      const int f = i / G;
+      const int g = i - f * G;
+      const size_t off = static_cast<size_t>(r0 + m0 + (f >> 1)) * I + 32 * g;
+      stage_frag(((f & 1) ? ws.act_lo : ws.act_hi) + off, frags + i * kFragDwords);
+    }
+    __syncthreads();
+    stream_expert<false, NA>(bufs, geo, H, I, H, b0, b1, frags, mc, r0 + m0, nullptr, nullptr,
+                             args.y);
+  }
 }
 
-// Rows per thread: the largest of 4, 2, 1 (at least min_rt) that still gives
-// >= 512 workgroups, else the smallest allowed.
-template <typename TilesFn>
-int pick_rows_per_thread(int min_rt, int slots, TilesFn tiles_for) {
-  int rt = 4;
-  while (rt > min_rt && static_cast<long long>(slots) * tiles_for(rt) < 512) rt >>= 1;
-  return rt;
+// ----------------------------------------------------------------- host -----
+// Lanes per row: the largest power of two <= 8 that divides G.
+int cluster_lanes(int G) {
+  int C = 1;
+  while (C < 8 && G % (2 * C) == 0) C *= 2;
+  return C;
 }
 
-size_t chunk_lds_bytes(int threads, int rows, int RT, int slots_per_row) {
-  return (static_cast<size_t>(threads) * RT * slots_per_row +
-          static_cast<size_t>(rows) * slots_per_row) * sizeof(float);
+template <typename Kernel>
+int resident_workgroups(Kernel kernel, size_t lds) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return per_cu * cus;
+}
+
+// Spread each active-expert slot's blocks over as many waves as the chip
+// holds at once (no second round), each wave taking a contiguous run.
+void split_blocks(Geom& geo, int slots, int resident) {
+  int splits = max(1, resident / max(1, slots));
+  splits = min(splits, (geo.nb + kWaves - 1) / kWaves);
+  geo.bpw = (geo.nb + splits * kWaves - 1) / (splits * kWaves);
+  geo.splits = (geo.nb + geo.bpw * kWaves - 1) / (geo.bpw * kWaves);
+}
+
+template <int NA>
+void launch_gate_up_na(const GateUpArgs& a, const FfnWorkspace& ws, Geom geo, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(NA) * geo.G * kFragDwords * sizeof(uint32_t);
+  const int slots = min(a.E, a.T * a.top_k);
+  split_blocks(geo, slots, resident_workgroups(gate_up_decode_kernel<NA>, lds));
+  hipLaunchKernelGGL((gate_up_decode_kernel<NA>), dim3(static_cast<unsigned>(slots) * geo.splits),
+                     dim3(kThreads), lds, stream, a, ws, geo);
+}
+
+template <int NA>
+void launch_down_na(const DownArgs& a, const FfnWorkspace& ws, Geom geo, hipStream_t stream) {
+  const size_t lds = static_cast<size_t>(2 * NA) * geo.G * kFragDwords * sizeof(uint32_t);
+  const int slots = min(a.E, a.T * a.top_k);
+  split_blocks(geo, slots, resident_workgroups(down_decode_kernel<NA>, lds));
+  hipLaunchKernelGGL((down_decode_kernel<NA>), dim3(static_cast<unsigned>(slots) * geo.splits),
+                     dim3(kThreads), lds, stream, a, ws, geo);
 }
 
 }  // namespace
 
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
-  const int G = a.H / kGroup;
-  const int P = row_phases(G);
-  const int threads = G * P;
-  const int slots = min(a.E, a.T * a.top_k);
-  auto tiles_for = [&](int rt) {
-    const int nt = P * rt / 2;
-    return (a.I + nt - 1) / nt;
-  };
-  const int RT = pick_rows_per_thread(P == 1 ? 2 : 1, slots, tiles_for);
-  const int NAMAX = a.T == 1 ? 1 : 2;
-  const int NT = P * RT / 2;
-  const int n_tiles = tiles_for(RT);
-  const size_t lds = chunk_lds_bytes(threads, P * RT, RT, NAMAX);
-  const dim3 grid(static_cast<unsigned>(slots) * n_tiles);
-#define MOE_GU(rt, na)                                                                  \
-  hipLaunchKernelGGL((gate_up_decode_kernel<rt, na>), grid, dim3(threads), lds, stream, a, ws, G, \
-                     P, NT, n_tiles)
-  if (NAMAX == 1) {
-    switch (RT) {
-      case 4: MOE_GU(4, 1); break;
-      case 2: MOE_GU(2, 1); break;
-      default: MOE_GU(1, 1); break;
-    }
-  } else {
-    switch (RT) {
-      case 4: MOE_GU(4, 2); break;
-      case 2: MOE_GU(2, 2); break;
-      default: MOE_GU(1, 2); break;
-    }
-  }
-#undef MOE_GU
+  Geom geo;
+  geo.G = a.H / kGroup;
+  geo.C = cluster_lanes(geo.G);
+  geo.spb = (geo.G + geo.C - 1) / geo.C;
+  const int half = (64 / geo.C) / 2;  // gate (= up) rows per block
+  geo.nb = (a.I + half - 1) / half;
+  if (a.T == 1)
+    launch_gate_up_na<1>(a, ws, geo, stream);
+  else
+    launch_gate_up_na<2>(a, ws, geo, stream);
 }
 
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
-  const int G = a.I / kGroup;
-  const int P = row_phases(G);
-  const int threads = G * P;
-  const int slots = min(a.E, a.T * a.top_k);
-  auto tiles_for = [&](int rt) { return (a.H + P * rt - 1) / (P * rt); };
-  const int RT = pick_rows_per_thread(1, slots, tiles_for);
-  const int MRMAX = a.T == 1 ? 1 : 2;
-  const int n_tiles = tiles_for(RT);
-  const size_t lds = chunk_lds_bytes(threads, P * RT, RT, MRMAX);
-  const dim3 grid(static_cast<unsigned>(slots) * n_tiles);
-#define MOE_DN(rt, mr)                                                                          \
-  hipLaunchKernelGGL((down_decode_kernel<rt, mr>), grid, dim3(threads), lds, stream, a, ws, G, P, \
-                     n_tiles)
-  if (MRMAX == 1) {
-    switch (RT) {
-      case 4: MOE_DN(4, 1); break;
-      case 2: MOE_DN(2, 1); break;
-      default: MOE_DN(1, 1); break;
-    }
-  } else {
-    switch (RT) {
-      case 4: MOE_DN(4, 2); break;
-      case 2: MOE_DN(2, 2); break;
-      default: MOE_DN(1, 2); break;
-    }
-  }
-#undef MOE_DN
+  Geom geo;
+  geo.G = a.I / kGroup;
+  geo.C = cluster_lanes(geo.G);
+  geo.spb = (geo.G + geo.C - 1) / geo.C;
+  geo.nb = (a.H + 64 / geo.C - 1) / (64 / geo.C);
+  if (a.T == 1)
+    launch_down_na<1>(a, ws, geo, stream);
+  else
+    launch_down_na<2>(a, ws, geo, stream);
 }
 
 }  // namespace moe
