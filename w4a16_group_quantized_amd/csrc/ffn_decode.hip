@@ -42,7 +42,7 @@ namespace {
 constexpr uint32_t kOnes = 0x3C003C00u;   // fp16 1.0 in both halves
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kDepth = 8;                 // weight loads in flight per lane (ring slots)
+constexpr int kDepth = 4;                 // weight loads in flight per lane (ring slots)
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for raw dword access on gfx9
 constexpr int kFragDwords = 20;           // LDS dwords per (A row, group): 16 pairs, c1, s, pad
 
@@ -196,31 +196,60 @@ __device__ __forceinline__ int block_row(int b, int k, int R, int I, int H) {
 }
 
 // ------------------------------------------------------------------ kernel --
-// Streams blocks [b0, b1) of one expert for mc (<= NA) rows of A.  Stage 2
-// fragments come in (hi, lo) pairs: fragment 2m is act_hi of row m, 2m + 1
-// its act_lo.
+// Per-wave step geometry of one run of blocks [b0, b1).
+struct WaveRun {
+  int k, lc, R, S, b0;
+};
+
+__device__ __forceinline__ WaveRun wave_run(const Geom& geo, int b0, int b1) {
+  const int lane = threadIdx.x & 63;
+  WaveRun w;
+  w.R = 64 / geo.C;
+  w.k = lane / geo.C;
+  w.lc = lane & (geo.C - 1);
+  w.S = (b1 - b0) * geo.spb;
+  w.b0 = b0;
+  return w;
+}
+
+// Issue the loads of step s into a slot (a no-load when s is past the run).
+template <bool GATE_UP>
+__device__ __forceinline__ void load_step(const ExpertBufs& bufs, const Geom& geo, const WaveRun& w,
+                                          int rows_w, int I, int H, int s, Slot& slot) {
+  const int gg = (s % geo.spb) * geo.C + w.lc;
+  const bool live = s < w.S && gg < geo.G;
+  const uint32_t row = live ? block_row<GATE_UP>(w.b0 + s / geo.spb, w.k, w.R, I, H) : rows_w;
+  load_slot(bufs, geo.G, row, live ? gg : 0, slot);
+}
+
+// Fill the ring with the first kDepth steps.  Needs only the expert, so it
+// is issued before the A rows are staged.
+template <bool GATE_UP>
+__device__ __forceinline__ void prime_ring(const ExpertBufs& bufs, const Geom& geo,
+                                           const WaveRun& w, int rows_w, int I, int H,
+                                           Slot (&ring)[kDepth]) {
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) load_step<GATE_UP>(bufs, geo, w, rows_w, I, H, d, ring[d]);
+}
+
+// Streams the wave's run of blocks for mc (<= NA) rows of A, the ring already
+// primed.  Stage 2 fragments come in (hi, lo) pairs: fragment 2m is act_hi of
+// row m, 2m + 1 its act_lo.
 template <bool GATE_UP, int NA>
-__device__ __forceinline__ void stream_expert(const ExpertBufs& bufs, const Geom& geo, int rows_w,
-                                              int I, int H, int b0, int b1, const uint32_t* frags,
-                                              int mc, int r_first, uint16_t* act_hi,
-                                              uint16_t* act_lo, float* y) {
+__device__ __forceinline__ void stream_expert(const ExpertBufs& bufs, const Geom& geo,
+                                              const WaveRun& wr, Slot (&ring)[kDepth], int rows_w,
+                                              int I, int H, const uint32_t* frags, int mc,
+                                              int r_first, uint16_t* act_hi, uint16_t* act_lo,
+                                              float* y) {
   const int lane = threadIdx.x & 63;
   const int C = geo.C;
-  const int R = 64 / C;
-  const int k = lane / C;
-  const int lc = lane & (C - 1);
+  const int R = wr.R;
+  const int k = wr.k;
+  const int lc = wr.lc;
   const int G = geo.G;
   const int spb = geo.spb;
-  const int S = (b1 - b0) * spb;
-
-  Slot ring[kDepth];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d) {
-    const int gg = (d % spb) * C + lc;
-    const bool live = d < S && gg < G;
-    const uint32_t row = live ? block_row<GATE_UP>(b0 + d / spb, k, R, I, H) : rows_w;
-    load_slot(bufs, G, row, live ? gg : 0, ring[d]);
-  }
+  const int S = wr.S;
+  const int b0 = wr.b0;
 
   constexpr int NF = GATE_UP ? NA : 2 * NA;  // fragments per chunk of A rows
   const int nf = GATE_UP ? mc : 2 * mc;
@@ -274,11 +303,7 @@ __device__ __forceinline__ void stream_expert(const ExpertBufs& bufs, const Geom
       }
       // Refill this slot with the step kDepth ahead; past the end this is a
       // no-load, issued anyway so every path keeps the same wait counts.
-      const int sn = s + kDepth;
-      const int gn = (sn % spb) * C + lc;
-      const bool live = sn < S && gn < G;
-      const uint32_t rown = live ? block_row<GATE_UP>(b0 + sn / spb, k, R, I, H) : rows_w;
-      load_slot(bufs, G, rown, live ? gn : 0, ring[d]);
+      load_step<GATE_UP>(bufs, geo, wr, rows_w, I, H, s + kDepth, ring[d]);
     }
   }
 }
@@ -301,11 +326,17 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(GateUpArgs arg
                                       args.sc + static_cast<size_t>(e) * rows_w * G,
                                       args.qz + static_cast<size_t>(e) * (rows_w / 8) * G,
                                       2 * I, G);
+  const WaveRun wr = wave_run(geo, b0, b1);
+  Slot ring[kDepth];
+  prime_ring<true>(bufs, geo, wr, 2 * I, I, H, ring);
   const int r0 = args.offsets[e];
   const int rows_e = args.offsets[e + 1] - r0;
   for (int m0 = 0; m0 < rows_e; m0 += NA) {
     const int mc = min(NA, rows_e - m0);
-    if (m0 > 0) __syncthreads();  // previous chunk's fragments are no longer read
+    if (m0 > 0) {
+      __syncthreads();  // previous chunk's fragments are no longer read
+      prime_ring<true>(bufs, geo, wr, 2 * I, I, H, ring);
+    }
     for (int i = threadIdx.x; i < mc * G; i += kThreads) {
       const int m = i / G;
       const int g = i - m * G;
@@ -313,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(GateUpArgs arg
       stage_frag(args.x + static_cast<size_t>(token) * H + 32 * g, frags + i * kFragDwords);
     }
     __syncthreads();
-    stream_expert<true, NA>(bufs, geo, 2 * I, I, H, b0, b1, frags, mc, r0 + m0, ws.act_hi,
+    stream_expert<true, NA>(bufs, geo, wr, ring, 2 * I, I, H, frags, mc, r0 + m0, ws.act_hi,
                             ws.act_lo, nullptr);
   }
 }
@@ -335,11 +366,17 @@ __global__ __launch_bounds__(kThreads) void down_decode_kernel(DownArgs args, Ff
   const ExpertBufs bufs = expert_bufs(args.qw + static_cast<size_t>(e) * rows_w * (G * 4),
                                       args.sc + static_cast<size_t>(e) * rows_w * G,
                                       args.qz + static_cast<size_t>(e) * (rows_w / 8) * G, H, G);
+  const WaveRun wr = wave_run(geo, b0, b1);
+  Slot ring[kDepth];
+  prime_ring<false>(bufs, geo, wr, H, I, H, ring);
   const int r0 = args.offsets[e];
   const int rows_e = args.offsets[e + 1] - r0;
   for (int m0 = 0; m0 < rows_e; m0 += NA) {
     const int mc = min(NA, rows_e - m0);
-    if (m0 > 0) __syncthreads();
+    if (m0 > 0) {
+      __syncthreads();
+      prime_ring<false>(bufs, geo, wr, H, I, H, ring);
+    }
     // fragment f = 2 m + {0: hi, 1: lo} of act row r0 + m0 + m, at f * G + g
     for (int i = threadIdx.x; i < 2 * mc * G; i += kThreads) {
       const int f = i / G;
@@ -348,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void down_decode_kernel(DownArgs args, Ff
       stage_frag(((f & 1) ? ws.act_lo : ws.act_hi) + off, frags + i * kFragDwords);
     }
     __syncthreads();
-    stream_expert<false, NA>(bufs, geo, H, I, H, b0, b1, frags, mc, r0 + m0, nullptr, nullptr,
+    stream_expert<false, NA>(bufs, geo, wr, ring, H, I, H, frags, mc, r0 + m0, nullptr, nullptr,
                              args.y);
   }
 }
