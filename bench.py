@@ -53,7 +53,24 @@ def parse_args(argv=None):
     p.add_argument("--no-graph", action="store_true", help="report the eager loop as value")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-repeats", type=int, default=3)
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB a few times (counter calibration)")
     return p.parse_args(argv)
+
+
+def copy_probe(mib: int) -> int:
+    """A plain copy kernel of known size, for scaling HBM byte counters."""
+    import torch
+
+    n = mib << 20
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "dispatches": 4}),
+          flush=True)
+    return 0
 
 
 # --------------------------------------------------------------------------- #
@@ -78,6 +95,47 @@ def layer_work(shape, num_active: int) -> dict:
         "flops": 6 * shape.T * shape.top_k * shape.H * shape.I,
         "gate_up_flops": 4 * shape.T * shape.top_k * shape.H * shape.I,
     }
+
+
+# --------------------------------------------------------------------------- #
+# HBM traffic from rocprofv3 counters (committed summary, valid for one source)
+# --------------------------------------------------------------------------- #
+KERNEL_SOURCES = {
+    "gate_up": "w4a16_group_quantized_amd/csrc/ffn_decode.hip",
+    "down": "w4a16_group_quantized_amd/csrc/ffn_decode.hip",
+}
+
+
+def source_sha256(rel: str) -> str:
+    import hashlib
+
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counter_traffic(workload: str, kernel: str):
+    """Bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary.
+
+    profiles/counters_<workload>.md holds lines
+      traffic <kernel> fetch_kib=F write_kib=W fetch_scale=a write_scale=b source_sha256=S
+    where a and b scale each counter to bytes moved by a plain copy of known
+    size.  The figure is returned only while the kernel source still hashes
+    to S (otherwise the kernel changed since the counters were taken: None).
+    """
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) < 2 or parts[0] != "traffic" or parts[1] != kernel:
+            continue
+        kv = dict(p.split("=", 1) for p in parts[2:])
+        if kv.get("source_sha256") != source_sha256(KERNEL_SOURCES[kernel]):
+            return None
+        fetch = float(kv["fetch_kib"]) * float(kv["fetch_scale"]) * 1024
+        write = float(kv["write_kib"]) * float(kv["write_scale"]) * 1024
+        return fetch + write
+    return None
 
 
 # --------------------------------------------------------------------------- #
@@ -125,6 +183,8 @@ def cpu_baseline(host: dict, shape, repeats: int) -> dict:
 # --------------------------------------------------------------------------- #
 def main(argv=None) -> int:
     args = parse_args(argv)
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build runs the MoE layer on a single MI355X "
@@ -199,6 +259,27 @@ def main(argv=None) -> int:
         f"gate_up {seg_ms[1] * 1e3:.1f}, down {seg_ms[2] * 1e3:.1f}, combine {seg_ms[3] * 1e3:.1f} us")
     assert torch.equal(layer.out, ref_out), "eager steps disagree"
 
+    # The dominant kernels alone: back-to-back launches on the routing of the
+    # batch (left in the layer's buffers), each on the next weight copy.
+    def kernel_avg_ms(launch) -> float:
+        for i in range(4):
+            launch(i)
+        k0 = torch.cuda.Event(enable_timing=True)
+        k1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        k0.record(stream)
+        for i in range(args.steps):
+            launch(i)
+        k1.record(stream)
+        torch.cuda.synchronize()
+        return k0.elapsed_time(k1) / args.steps
+
+    gate_up_ms = kernel_avg_ms(lambda i: ops.moe_w4a16_gate_up(
+        x, shape.top_k, layer.perm, copies[i % args.layers], layer.ffn_ws))
+    down_ms = kernel_avg_ms(lambda i: ops.moe_w4a16_down(
+        shape.T, shape.top_k, layer.perm, copies[i % args.layers], layer.y_sorted, layer.ffn_ws))
+    log(f"back-to-back: gate_up {gate_up_ms * 1e3:.1f} us, down {down_ms * 1e3:.1f} us")
+
     # HIP graphs: one captured step per weight copy, replayed round-robin
     graph_ms = None
     if not args.no_graph:
@@ -232,8 +313,23 @@ def main(argv=None) -> int:
 
     ms = graph_ms if graph_ms is not None else eager_ms
     tokens_per_s = shape.T / (ms * 1e-3)
-    gate_up_s = seg_ms[1] * 1e-3
-    achieved = work["gate_up_bytes"] / gate_up_s / 1e9
+    gate_up_s = gate_up_ms * 1e-3
+    intensity = work["gate_up_flops"] / work["gate_up_bytes"]
+    ridge = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": work["gate_up_bytes"] / gate_up_s / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": work["gate_up_flops"] / gate_up_s / 1e12,
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = counter_traffic(args.workload, "gate_up")
+    roof.update({
+        "kernel": "gate/up kernel of moe_w4a16_gate_up",
+        "avg_launch_us": gate_up_ms * 1e3,
+        "algorithmic_bytes_per_launch": work["gate_up_bytes"],
+        "algorithmic_flops_per_launch": work["gate_up_flops"],
+    })
     result = {
         "metric": "MoE layer tokens/s (decode: HBM GB/s of the gate/up kernel in roofline)",
         "value": tokens_per_s,
@@ -253,17 +349,7 @@ def main(argv=None) -> int:
             "group_size": 32, "weight_copies": args.layers, "active_experts": num_active,
             "timing": "hip-graph replay" if graph_ms is not None else "eager",
         },
-        "roofline": {
-            "kernel": "gate_up_decode_kernel (moe_w4a16_gate_up)",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "avg_launch_us": seg_ms[1] * 1e3,
-            "algorithmic_bytes_per_launch": work["gate_up_bytes"],
-        },
+        "roofline": roof,
         "layer": {
             "eager_us_per_step": eager_ms * 1e3,
             "graph_us_per_step": graph_ms * 1e3 if graph_ms is not None else None,
@@ -275,7 +361,9 @@ def main(argv=None) -> int:
             "mfma_frac": work["flops"] / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
             "segments_us": {"route+permute": seg_ms[0] * 1e3, "gate_up": seg_ms[1] * 1e3,
                             "down": seg_ms[2] * 1e3, "combine": seg_ms[3] * 1e3},
-            "down_GBps": work["down_bytes"] / (seg_ms[2] * 1e-3) / 1e9,
+            "down_kernel_us": down_ms * 1e3,
+            "down_GBps": work["down_bytes"] / (down_ms * 1e-3) / 1e9,
+            "down_traffic": counter_traffic(args.workload, "down"),
         },
     }
     if not args.no_cpu_baseline:
