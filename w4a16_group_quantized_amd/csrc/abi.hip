@@ -141,7 +141,13 @@ int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t
   a.qw = w13_qweight;
   a.sc = w13_scales;
   a.qz = w13_qzeros;
-  launch_gate_up_decode(a, ws, static_cast<hipStream_t>(stream));
+  if (T <= kDecodeMaxT) {
+    launch_gate_up_decode(a, ws, static_cast<hipStream_t>(stream));
+  } else {
+    launch_build_tiles(expert_offsets, active_experts, num_active, ws,
+                       static_cast<hipStream_t>(stream));
+    launch_gate_up_prefill(a, ws, static_cast<hipStream_t>(stream));
+  }
   return check_launch();
 }
 
@@ -173,7 +179,10 @@ int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
   a.sc = w2_scales;
   a.qz = w2_qzeros;
   a.y = y_sorted;
-  launch_down_decode(a, ws, static_cast<hipStream_t>(stream));
+  if (T <= kDecodeMaxT)
+    launch_down_decode(a, ws, static_cast<hipStream_t>(stream));
+  else
+    launch_down_prefill(a, ws, static_cast<hipStream_t>(stream));  // tile list from gate_up
   return check_launch();
 }
 

@@ -59,6 +59,14 @@ struct DownArgs {
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 
+// Matrix-core variant: a tile list (built from the routing into the FFN
+// workspace) followed by the two grouped GEMMs.
+int prefill_max_tiles(int64_t S, int E);
+void launch_build_tiles(const int* offsets, const int* active, const int* num_active,
+                        const FfnWorkspace& ws, hipStream_t stream);
+void launch_gate_up_prefill(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
+void launch_down_prefill(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
+
 void launch_combine(const float* y_sorted, const float* weights,
                     const int* slot_rows, int T, int top_k, int H,
                     uint16_t* out, hipStream_t stream);
