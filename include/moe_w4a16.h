@@ -51,7 +51,8 @@
  * w13 has N = 2I, K = H (rows [0, I) gate, [I, 2I) up); w2 has N = H, K = I.
  *
  * Limits: 1 <= E <= 4096; 1 <= top_k <= min(E, 64); S < 2^31; group_size == 32;
- * H and I multiples of 32 with 32 <= H, I <= 16384.
+ * H and I multiples of 32 with 32 <= H, I <= 16384; T * H < 2^31 (x is
+ * addressed with 32-bit byte offsets).
  */
 #ifndef MOE_W4A16_H_
 #define MOE_W4A16_H_

@@ -99,6 +99,8 @@ def test_ffn_rejects_bad_arguments():
     assert _ffn(lib, x=FAKE + 8) == ops.MOE_ERR_INVALID_ARG
     assert _ffn(lib, T=0, x=None, y=None) == ops.MOE_OK
     assert _ffn(lib, k=11, E=10) == ops.MOE_ERR_INVALID_ARG
+    # x is addressed with 32-bit byte offsets: T * H < 2^31
+    assert _ffn(lib, T=(1 << 31) // 2560 + 1, k=1) == ops.MOE_ERR_UNSUPPORTED
 
 
 def test_gate_up_and_down_reject_bad_arguments():

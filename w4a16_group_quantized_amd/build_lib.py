@@ -28,6 +28,9 @@ FLAGS = [
     "-Wno-unused-function",
     # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-instruction results in ordinary vector registers, which the fp32
+    # scaling reads directly (no accumulation-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -38,21 +38,29 @@ int check_dims(int32_t H, int32_t I, int32_t group_size) {
 
 namespace moe {
 
-size_t ffn_workspace_bytes(int64_t S, int E, int I) {
-  const size_t act = align256(static_cast<size_t>(S) * I * sizeof(uint16_t));
-  const size_t tiles = align256((static_cast<size_t>(S) + E + 1) * 2 * sizeof(int));
-  return 2 * act + tiles + 256;
+// Layout: act_hi | act_lo | tile list | tile count | permuted x, each part
+// 256-byte aligned.  The tile list holds at most S + E entries (every tile
+// but one per expert is full).
+size_t ffn_workspace_bytes(int64_t T, int top_k, int E, int H, int I) {
+  const size_t S = static_cast<size_t>(T) * top_k;
+  const size_t act = align256(S * I * sizeof(uint16_t));
+  const size_t tiles = align256((S + E + 1) * 2 * sizeof(int));
+  const size_t xp = align256(static_cast<size_t>(T) * H * sizeof(uint16_t));
+  return 2 * act + tiles + 256 + xp;
 }
 
-FfnWorkspace ffn_workspace_carve(void* base, int64_t S, int E, int I) {
+FfnWorkspace ffn_workspace_carve(void* base, int64_t T, int top_k, int E, int H, int I) {
   char* p = static_cast<char*>(base);
-  const size_t act = align256(static_cast<size_t>(S) * I * sizeof(uint16_t));
-  const size_t tiles = align256((static_cast<size_t>(S) + E + 1) * 2 * sizeof(int));
+  const size_t S = static_cast<size_t>(T) * top_k;
+  const size_t act = align256(S * I * sizeof(uint16_t));
+  const size_t tiles = align256((S + E + 1) * 2 * sizeof(int));
   FfnWorkspace ws;
   ws.act_hi = reinterpret_cast<uint16_t*>(p);
   ws.act_lo = reinterpret_cast<uint16_t*>(p + act);
   ws.tiles = reinterpret_cast<int*>(p + 2 * act);
   ws.tile_count = reinterpret_cast<int*>(p + 2 * act + tiles);
+  ws.x_perm = reinterpret_cast<uint16_t*>(p + 2 * act + tiles + 256);
+  (void)H;
   return ws;
 }
 
@@ -108,7 +116,7 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
 
 size_t moe_ffn_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
   if (check_routing(T, top_k, E) != MOE_OK || check_dims(H, I, kGroup) != MOE_OK) return 0;
-  return ffn_workspace_bytes(T * top_k, E, I);
+  return ffn_workspace_bytes(T, top_k, E, H, I);
 }
 
 int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t* expert_offsets,
@@ -119,14 +127,14 @@ int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t
                       void* stream) {
   if (int st = check_routing(T, top_k, E)) return st;
   if (int st = check_dims(H, I, group_size)) return st;
+  if (T * static_cast<int64_t>(H) >= (static_cast<int64_t>(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(expert_offsets) || !ok_ptr(sorted_slots) || !ok_ptr(active_experts) ||
       !ok_ptr(num_active) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) || !ok_ptr(w13_qzeros) ||
       !ok_ptr(workspace))
     return MOE_ERR_INVALID_ARG;
-  const int64_t S = T * top_k;
-  if (workspace_bytes < ffn_workspace_bytes(S, E, I)) return MOE_ERR_WORKSPACE;
-  const FfnWorkspace ws = ffn_workspace_carve(workspace, S, E, I);
+  if (workspace_bytes < ffn_workspace_bytes(T, top_k, E, H, I)) return MOE_ERR_WORKSPACE;
+  const FfnWorkspace ws = ffn_workspace_carve(workspace, T, top_k, E, H, I);
   GateUpArgs a;
   a.x = x;
   a.T = static_cast<int>(T);
@@ -144,8 +152,8 @@ int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t
   if (T <= kDecodeMaxT) {
     launch_gate_up_decode(a, ws, static_cast<hipStream_t>(stream));
   } else {
-    launch_build_tiles(expert_offsets, active_experts, num_active, ws,
-                       static_cast<hipStream_t>(stream));
+    launch_prefill_prep(x, static_cast<int>(T), H, expert_offsets, active_experts, num_active,
+                        T * top_k, E, ws, static_cast<hipStream_t>(stream));
     launch_gate_up_prefill(a, ws, static_cast<hipStream_t>(stream));
   }
   return check_launch();
@@ -163,9 +171,8 @@ int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
       !ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) || !ok_ptr(y_sorted) ||
       !ok_ptr(workspace))
     return MOE_ERR_INVALID_ARG;
-  const int64_t S = T * top_k;
-  if (workspace_bytes < ffn_workspace_bytes(S, E, I)) return MOE_ERR_WORKSPACE;
-  const FfnWorkspace ws = ffn_workspace_carve(workspace, S, E, I);
+  if (workspace_bytes < ffn_workspace_bytes(T, top_k, E, H, I)) return MOE_ERR_WORKSPACE;
+  const FfnWorkspace ws = ffn_workspace_carve(workspace, T, top_k, E, H, I);
   DownArgs a;
   a.T = static_cast<int>(T);
   a.top_k = top_k;

@@ -31,9 +31,10 @@ struct FfnWorkspace {
   uint16_t* act_lo;  // [S, I] fp16, act - act_hi rounded to fp16
   int* tiles;        // matrix-core M-tile list (prefill variant)
   int* tile_count;   // number of valid entries of `tiles`
+  uint16_t* x_perm;  // [T, H] x in k-slot order (prefill variant)
 };
-size_t ffn_workspace_bytes(int64_t S, int E, int I);
-FfnWorkspace ffn_workspace_carve(void* base, int64_t S, int E, int I);
+size_t ffn_workspace_bytes(int64_t T, int top_k, int E, int H, int I);
+FfnWorkspace ffn_workspace_carve(void* base, int64_t T, int top_k, int E, int H, int I);
 
 struct GateUpArgs {
   const uint16_t* x;
@@ -59,11 +60,15 @@ struct DownArgs {
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 
-// Matrix-core variant: a tile list (built from the routing into the FFN
-// workspace) followed by the two grouped GEMMs.
-int prefill_max_tiles(int64_t S, int E);
-void launch_build_tiles(const int* offsets, const int* active, const int* num_active,
-                        const FfnWorkspace& ws, hipStream_t stream);
+// Matrix-core variant: a prep kernel (tile list built from the routing, x
+// permuted to k-slot order, both into the FFN workspace) followed by the two
+// grouped GEMMs.  prefill_msub is the number of 32-row subtiles per M-tile
+// for S = T * top_k sorted rows over E experts.
+int prefill_msub(int64_t S, int E);
+int64_t prefill_max_tiles(int64_t S, int E);
+void launch_prefill_prep(const uint16_t* x, int T, int H, const int* offsets, const int* active,
+                         const int* num_active, int64_t S, int E, const FfnWorkspace& ws,
+                         hipStream_t stream);
 void launch_gate_up_prefill(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 void launch_down_prefill(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 

@@ -5,27 +5,40 @@
 // active experts' multi-row segments; group size 32 along K):
 //   stage 1: act[r, c] = SiLU(h_gate) * h_up,  h = x[token(r)] . W13[e]^T
 //   stage 2: y_sorted[r, n] = act[r] . W2[e]^T
-// but as dense tiles on v_mfma_f32_16x16x32_f16.
+// as dense tiles on v_mfma_f32_32x32x16_f16.
 //
-// Schedule.  A tile-list kernel cuts every active expert's segment of sorted
-// rows into M-tiles of kBM rows (so a heavily loaded expert becomes many
-// tiles) and the GEMM grid is (M-tile slot, N-tile); slots past the list
-// exit at once.  Consecutive workgroups share an M-tile, and the M-tiles of
-// one expert are consecutive, so the tiles reading the same weights run at
-// about the same time.
+// Schedule.  A tile list cuts every active expert's segment of sorted rows
+// into M-tiles of MSUB * 32 rows (a heavily loaded expert becomes many tiles).
+// A workgroup computes one M-tile against an N-tile of 128 weight rows; each
+// of its 4 waves owns 32 weight rows and all of the M-tile's rows, so one
+// dequantised weight fragment feeds MSUB matrix instructions.  Work items
+// are numbered M-tile-major and every XCD takes a contiguous run of them, so
+// the workgroups of one XCD share the A rows of an M-tile and, one expert at a
+// time, that expert's weights in their L2.
 //
-// Operands.  One MFMA covers exactly one quantisation group (K = 32), so each
-// group's product P = A . (q - z) is formed with an exact integer B (q - z is
-// an integer in [-15, 15], exact in fp16) and a zero accumulator, then
-// scaled in fp32: acc += s[n, g] * P.  A lane holds 8 values of a row of A
-// and 8 of a column of B over the same k-slots; within each 8-wide block the
-// k order is (0, 4, 1, 5, 2, 6, 3, 7), the order in which the nibble unpack
-// produces (q - z) pairs, so A is stored permuted the same way.  Stage 2 runs
-// act_hi and act_lo through two MFMAs into the same partial, carrying act at
-// about 22 bits.  Inputs are staged in LDS two groups at a time, double
-// buffered; weights are read with buffer loads so rows past the matrix read
-// as zeros.
+// Operands.  One quantisation group (K = 32) is two MFMAs chained into a
+// partial P = A . (q - z) with an exact integer B (q - z is an integer in
+// [-15, 15], exact in fp16) and a zero accumulator; P is then scaled in fp32:
+// acc += s[n, g] * P.  Rounding the dequantised weight to fp16 instead would
+// cost as much precision as rounding act to fp16, which the layer tolerance
+// does not allow.  Within each 8-wide k block the k order is
+// (0, 4, 1, 5, 2, 6, 3, 7), the order in which the nibble unpack produces
+// (q - z) pairs, so A is stored permuted the same way: x by a pre-pass, act
+// by the stage-1 epilogue.  A lane of half h of the wave supplies, for MFMA t
+// of a group, 8-value block 2h + t.  The two wave halves load the codes of
+// two consecutive groups (16 bytes per lane), and two v_permlane32_swap
+// exchanges give every lane its two blocks of each group.  Stage 2 runs
+// act_hi and act_lo through the same partial (act carried at about 22 bits).
+//
+// Staging.  A rows go through LDS in fragment order (one 1 KiB block per
+// (group, 32-row subtile, MFMA), lane L at byte 16 L, so every fragment read
+// is one contiguous ds_read_b128 per lane), kKC groups per stage, double
+// buffered; weights, zeros and scales are read by each lane straight into
+// registers with buffer loads (out-of-range reads return zeros), one stage
+// ahead.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 
@@ -33,30 +46,47 @@ namespace moe {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float float4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float float16v __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 64;                    // rows of A per M-tile
-constexpr int kBN = 128;                   // weight rows (output columns) per N-tile
-constexpr int kThreads = 256;              // 4 waves: 2 (M) x 2 (N)
-constexpr int kKC = 2;                     // groups per LDS stage
-constexpr int kAStride = kKC * 32 + 8;     // halfs per staged A row (padded)
+constexpr int kSub = 32;                   // MFMA tile edge
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBN = kWaves * kSub;         // weight rows per N-tile
+constexpr int kBlockHalfs = 64 * 8;        // one fragment block: 64 lanes x 8 fp16
 constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3 for raw dword access on gfx9
-constexpr int kBStride = kBN + 16;         // dwords per (group, word) row of staged codes (bank spread)
+
+template <bool GATE_UP>
+struct StageCfg {
+  static constexpr int kCopies = GATE_UP ? 1 : 2;   // A copies: x, or act hi + lo
+  static constexpr int kKC = GATE_UP ? 4 : 2;       // groups per LDS stage
+};
 
 struct PrefillArgs {
-  const uint16_t* x;   // stage 1 A source
+  const uint16_t* a_hi;        // stage 1: permuted x [T, H]; stage 2: act_hi [S, I]
+  const uint16_t* a_lo;        // stage 2: act_lo [S, I]
+  const int* sorted_slots;     // stage 1 row gather
   int T, top_k, E, H, I;
   const int* offsets;
-  const int* sorted_slots;
+  const int* tiles;
+  const int* tile_count;
   const int* qw;
   const uint16_t* sc;
   const int* qz;
-  float* y;            // stage 2 output
+  uint16_t* act_hi;            // stage 1 outputs
+  uint16_t* act_lo;
+  float* y;                    // stage 2 output
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
                                            kBufferFlags);
+}
+
+// Position of column c once its 8-wide block is permuted to k-slot order
+// (0, 4, 1, 5, 2, 6, 3, 7).
+__device__ __forceinline__ int slot_pos(int c) {
+  return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1);
 }
 
 // 8 consecutive fp16 (4 dwords: (a0,a1) (a2,a3) (a4,a5) (a6,a7)) reordered
@@ -66,21 +96,17 @@ __device__ __forceinline__ uint4 permute8(uint4 d) {
                     (d.y & 0xFFFFu) | (d.w << 16), (d.y >> 16) | (d.w & 0xFFFF0000u));
 }
 
-// (q - z) of one packed word as 8 fp16 in k-slot order, exactly.
-__device__ __forceinline__ half8 exact_codes(uint32_t w, uint32_t z) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+// (q - z) of one packed word as 8 fp16 in k-slot order, exactly.  m1024 holds
+// -(1024 + z) and m64 holds -(64 + z) in both halves.
+__device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t bias, h2 m1024, h2 m64) {
   const uint32_t w8 = w >> 8;
-  const uint32_t bias = 0x64006400u;
   const h2 pa = __builtin_bit_cast(h2, (w & 0x000F000Fu) | bias);   // 1024 + q0, 1024 + q4
   const h2 pb = __builtin_bit_cast(h2, (w & 0x00F000F0u) | bias);   // 1024 + 16 q1, ...
   const h2 pc = __builtin_bit_cast(h2, (w8 & 0x000F000Fu) | bias);  // 1024 + q2, 1024 + q6
   const h2 pd = __builtin_bit_cast(h2, (w8 & 0x00F000F0u) | bias);  // 1024 + 16 q3, ...
-  const _Float16 zf = static_cast<_Float16>(static_cast<float>(z));
-  const h2 m1024 = {static_cast<_Float16>(-1024.f) - zf, static_cast<_Float16>(-1024.f) - zf};
-  const h2 m64 = {static_cast<_Float16>(-64.f) - zf, static_cast<_Float16>(-64.f) - zf};
   const h2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-  const h2 r0 = pa + m1024;              // q0 - z, q4 - z (exact)
-  const h2 r1 = pb * sixteenth + m64;    // q1 - z, q5 - z (exact)
+  const h2 r0 = pa + m1024;              // q0 - z, q4 - z
+  const h2 r1 = pb * sixteenth + m64;    // q1 - z, q5 - z
   const h2 r2 = pc + m1024;
   const h2 r3 = pd * sixteenth + m64;
   half8 out;
@@ -89,159 +115,358 @@ __device__ __forceinline__ half8 exact_codes(uint32_t w, uint32_t z) {
   return out;
 }
 
-// Shared-memory stage of both operands (one buffer of the double buffer).
-template <bool GATE_UP>
-struct Stage {
-  static constexpr int kARows = GATE_UP ? 1 : 2;           // A copies: x, or act hi/lo
-  uint16_t a[kARows][kBM * kAStride];                     // A rows, k-slot order
-  uint32_t bq[kKC * 4 * kBStride];                         // codes: [group][word][row]
-  uint16_t bs[kKC * kBN];                                  // scales: [group][row]
-  uint32_t bz[kKC * (kBN / 8)];                            // zero words: [group][row block]
+// Per-lane weight operands of one stage: codes of kKC / 2 group pairs (lane
+// half h loads group 2p + h of pair p), one zero word and one scale per group.
+template <int KC>
+struct BRegs {
+  uint4 q[KC / 2];
+  uint32_t z[KC];
+  uint32_t s[KC];
 };
 
-// Weight row of the N-tile's row r.  Stage 1: rows [0, 64) gate columns,
-// [64, 128) the matching up columns.
-template <bool GATE_UP>
-__device__ __forceinline__ int tile_weight_row(int nt, int r, int I) {
-  if (GATE_UP) return r < kBN / 2 ? nt * (kBN / 2) + r : I + nt * (kBN / 2) + (r - kBN / 2);
-  return nt * kBN + r;
+struct BAddr {
+  __amdgpu_buffer_rsrc_t rq, rs, rz;
+  uint32_t q_row, s_row, z_row;       // byte offsets of the lane's row (q_row: plus h * 16)
+  uint32_t q_oob, s_oob, z_oob;       // offsets that read as zero
+  int G;
+  int h;                              // lane half
+};
+
+// Loads of one stage's weight operands.  FULL: every group of the stage lies
+// inside the matrix (offsets are the row base plus constants); otherwise
+// groups past the end read zeros.  Both forms issue the same loads in the same
+// order, so the wait counts after either agree.
+template <int KC, bool FULL>
+__device__ __forceinline__ void load_b(const BAddr& ba, int g0, BRegs<KC>& b) {
+  const uint32_t q0 = ba.q_row + static_cast<uint32_t>(g0) * 16u;
+  const uint32_t z0 = ba.z_row + static_cast<uint32_t>(g0) * 4u;
+  const uint32_t s0 = ba.s_row + static_cast<uint32_t>(g0) * 2u;
+#pragma unroll
+  for (int pp = 0; pp < KC / 2; ++pp) {
+    // lane half h loads group g0 + 2 pp + h: ba.q_row already holds h * 16
+    const uint32_t off = FULL || g0 + 2 * pp + ba.h < ba.G ? q0 + pp * 32u : ba.q_oob;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rq, static_cast<int>(off), 0, 0);
+    b.q[pp] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+#pragma unroll
+  for (int g = 0; g < KC; ++g) {
+    const bool live = FULL || g0 + g < ba.G;
+    const uint32_t zo = live ? z0 + g * 4u : ba.z_oob;
+    const uint32_t so = live ? s0 + g * 2u : ba.s_oob;
+    b.z[g] = __builtin_amdgcn_raw_buffer_load_b32(ba.rz, static_cast<int>(zo), 0, 0);
+    b.s[g] = __builtin_amdgcn_raw_buffer_load_b16(ba.rs, static_cast<int>(so), 0, 0);
+  }
 }
 
-// Global loads of one stage into registers (issued before the previous
-// stage is computed).
-struct StageRegs {
-  uint4 a[2][2];   // [chunk][copy]
-  uint4 q;
-  uint32_t s;
-  uint32_t z;
+template <int KC>
+__device__ __forceinline__ void load_b_stage(const BAddr& ba, int g0, BRegs<KC>& b) {
+  if (g0 + KC <= ba.G) load_b<KC, true>(ba, g0, b);
+  else load_b<KC, false>(ba, g0, b);
+}
+
+// A staging.  8 threads share a row, so each load instruction reads 128
+// contiguous bytes of 8 rows; a pass of the 256 threads covers one 32-row
+// subtile, and each thread loads kCPP chunks of 16 bytes per pass.  A row's
+// stage span is kCopies x kKC groups x 4 chunks.  Rows past the tile read
+// past the end of the buffer (zeros, no traffic).
+template <bool GATE_UP, int MSUB>
+struct AStage {
+  static constexpr int kKC = StageCfg<GATE_UP>::kKC;
+  static constexpr int kCopies = StageCfg<GATE_UP>::kCopies;
+  static constexpr int kBM = MSUB * kSub;
+  static constexpr int kTPR = 8;                               // threads per row
+  static constexpr int kCPR = kCopies * kKC * 4;               // chunks per row per stage
+  static constexpr int kCPP = kCPR / kTPR;                     // chunks per thread per pass
+  static constexpr int kStageHalfs = kCopies * kKC * MSUB * 2 * kBlockHalfs;
+  static_assert(kThreads / kTPR == kSub, "one pass of the workgroup stages one subtile");
+  static_assert(kCPR % kTPR == 0, "stage chunks must split evenly over a row's threads");
+  uint4 v[MSUB][kCPP];
 };
 
-template <bool GATE_UP>
-__device__ __forceinline__ void load_stage(const PrefillArgs& p, const uint16_t* act_hi,
-                                           const uint16_t* act_lo, const int* a_rows, int rows,
-                                           int K, int N, int G, int g0,
-                                           __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rs,
-                                           __amdgpu_buffer_rsrc_t rz, int nt, StageRegs& st) {
-  const int t = threadIdx.x;
-  // A: kBM rows x kKC*32 k = 8 chunks of 8 halfs per row, 2 chunks per thread
+struct ASrc {
+  __amdgpu_buffer_rsrc_t r[2];   // copy 0 (x or act_hi), copy 1 (act_lo)
+  uint32_t row_off[4];           // byte offset of this thread's row of subtile i
+};
+
+// XOR applied to the 16-byte slot of a fragment block, so that the 8 threads
+// staging one row (chunk c of groups 2m and 2m + 1) write 8 different bank
+// groups, while the 8 lanes of any aligned octet still read distinct ones.
+__device__ __forceinline__ int slot_xor(int g, int h, int t) { return ((g & 1) << 2) | (h << 1) | t; }
+
+template <bool GATE_UP, int MSUB, int NS>
+__device__ __forceinline__ void load_a(const ASrc& src, int g0, AStage<GATE_UP, MSUB>& a) {
+  using S = AStage<GATE_UP, MSUB>;
+  const int t8 = threadIdx.x % S::kTPR;
+  const int soff = g0 * kGroup * 2;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int id = t + c * kThreads;
-    const int r = id >> 3;
-    const int ch = id & 7;
-    const int k = g0 * 32 + ch * 8;
-    const bool live = r < rows && k < K;
-    if (GATE_UP) {
-      st.a[c][0] = live ? *reinterpret_cast<const uint4*>(p.x + static_cast<size_t>(a_rows[r]) * K + k)
-                        : make_uint4(0u, 0u, 0u, 0u);
-    } else {
-      const size_t off = static_cast<size_t>(a_rows[r]) * K + k;
-      st.a[c][0] = live ? *reinterpret_cast<const uint4*>(act_hi + off) : make_uint4(0u, 0u, 0u, 0u);
-      st.a[c][1] = live ? *reinterpret_cast<const uint4*>(act_lo + off) : make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < NS; ++i)
+#pragma unroll
+    for (int k = 0; k < S::kCPP; ++k) {
+      const int cc = k * S::kTPR + t8;
+      const int cp = cc / (S::kKC * 4);
+      const int g = (cc / 4) % S::kKC;
+      const int c = cc % 4;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+          src.r[cp], static_cast<int>(src.row_off[i] + g * kGroup * 2 + c * 16), soff, 0);
+      a.v[i][k] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-  }
-  // B: kBN rows x kKC groups of 16 bytes, one per thread
-  const int r = t >> 1;
-  const int gl = t & 1;
-  const int g = g0 + gl;
-  const uint32_t n = static_cast<uint32_t>(tile_weight_row<GATE_UP>(nt, r, p.I));
-  // a group past G is loaded from one past the end of the buffers: zeros
-  const uint32_t idx = g < G ? __umul24(n, G) + g : static_cast<uint32_t>(N) * G;
-  const auto qv = __builtin_amdgcn_raw_buffer_load_b128(rq, static_cast<int>(idx * 16u), 0, 0);
-  st.q = make_uint4(qv[0], qv[1], qv[2], qv[3]);
-  st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, static_cast<int>(idx * 2u), 0, 0);
-  // zero words: kBN / 8 row blocks x kKC groups, threads 0..31
-  st.z = 0;
-  if (t < (kBN / 8) * kKC) {
-    const int rb = t >> 1;
-    const int zg = g0 + (t & 1);
-    const uint32_t n0 = static_cast<uint32_t>(tile_weight_row<GATE_UP>(nt, rb * 8, p.I));
-    if (zg < G)
-      st.z = __builtin_amdgcn_raw_buffer_load_b32(rz, static_cast<int>((__umul24(n0 >> 3, G) + zg) * 4u), 0, 0);
-  }
 }
 
-template <bool GATE_UP>
-__device__ __forceinline__ void store_stage(const StageRegs& st, Stage<GATE_UP>& sm) {
-  const int t = threadIdx.x;
+template <bool GATE_UP, int MSUB, int NS>
+__device__ __forceinline__ void store_a(const AStage<GATE_UP, MSUB>& a, uint16_t* stage) {
+  using S = AStage<GATE_UP, MSUB>;
+  const int j = threadIdx.x / S::kTPR;
+  const int t8 = threadIdx.x % S::kTPR;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int id = t + c * kThreads;
-    const int r = id >> 3;
-    const int ch = id & 7;
+  for (int i = 0; i < NS; ++i)
 #pragma unroll
-    for (int cp = 0; cp < Stage<GATE_UP>::kARows; ++cp)
-      *reinterpret_cast<uint4*>(&sm.a[cp][r * kAStride + ch * 8]) = permute8(st.a[c][cp]);
-  }
-  const int r = t >> 1;
-  const int gl = t & 1;
-  sm.bq[(gl * 4 + 0) * kBStride + r] = st.q.x;
-  sm.bq[(gl * 4 + 1) * kBStride + r] = st.q.y;
-  sm.bq[(gl * 4 + 2) * kBStride + r] = st.q.z;
-  sm.bq[(gl * 4 + 3) * kBStride + r] = st.q.w;
-  sm.bs[gl * kBN + r] = static_cast<uint16_t>(st.s);
-  if (t < (kBN / 8) * kKC) sm.bz[(t & 1) * (kBN / 8) + (t >> 1)] = st.z;
+    for (int k = 0; k < S::kCPP; ++k) {
+      const int cc = k * S::kTPR + t8;
+      const int cp = cc / (S::kKC * 4);
+      const int g = (cc / 4) % S::kKC;
+      const int c = cc % 4;
+      const int block = ((cp * S::kKC + g) * MSUB + i) * 2 + (c & 1);
+      const int slot = (32 * (c >> 1) + j) ^ slot_xor(g, c >> 1, c & 1);
+      *reinterpret_cast<uint4*>(stage + block * kBlockHalfs + slot * 8) = a.v[i][k];
+    }
 }
 
-// Wave tile: 2 M-subtiles (16 rows each) x 4 N-subtiles (16 weight rows each).
-// Stage 1: N-subtiles 0,1 are gate columns, 2,3 the matching up columns.
-template <bool GATE_UP>
-__device__ __forceinline__ int wave_nrow(int wn, int s) {
-  if (GATE_UP) return (s < 2 ? 0 : kBN / 2) + wn * 32 + (s & 1) * 16;
-  return wn * 64 + s * 16;
-}
-
-template <bool GATE_UP>
-__device__ __forceinline__ void compute_stage(const Stage<GATE_UP>& sm, int ngroups, int wm, int wn,
-                                              float4v (&acc)[2][4]) {
+// One stage of the main loop: NG groups (NG < kKC only in a tail stage) of a
+// tile with NS live 32-row subtiles.  The scaling of each partial is issued
+// after the next partial's MFMAs, so it does not wait on its own MFMA.
+template <bool GATE_UP, int MSUB, int NS, int NG>
+__device__ __forceinline__ void compute_stage(const uint16_t* stage,
+                                              const BRegs<StageCfg<GATE_UP>::kKC>& b,
+                                              uint32_t zshift, uint32_t bias,
+                                              float16v (&acc)[MSUB]) {
+  constexpr int KC = StageCfg<GATE_UP>::kKC;
+  constexpr int kLoOff = KC * MSUB * 2 * kBlockHalfs;   // act_lo copy
   const int lane = threadIdx.x & 63;
-  const int j = lane & 15;
-  const int q = lane >> 4;
-  for (int gl = 0; gl < ngroups; ++gl) {
-    half8 a[Stage<GATE_UP>::kARows][2];
+  float16v pend = {};
+  float pend_s = 0.f;
 #pragma unroll
-    for (int cp = 0; cp < Stage<GATE_UP>::kARows; ++cp)
+  for (int pp = 0; pp < (NG + 1) / 2; ++pp) {
+    // lane half 0 holds group 2pp, half 1 group 2pp + 1; after the swaps the
+    // lower half holds words 0 and 1 and the upper half words 2 and 3 of each
+    const auto sx = __builtin_amdgcn_permlane32_swap(b.q[pp].x, b.q[pp].z, false, false);
+    const auto sy = __builtin_amdgcn_permlane32_swap(b.q[pp].y, b.q[pp].w, false, false);
+    const uint32_t words[2][2] = {{sx[0], sy[0]}, {sx[1], sy[1]}};   // [group][MFMA]
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int row = wm * 32 + m * 16 + j;
-        a[cp][m] = __builtin_bit_cast(
-            half8, *reinterpret_cast<const uint4*>(&sm.a[cp][row * kAStride + gl * 32 + q * 8]));
-      }
-    float4v p[2][4];
-    float sc[4];
+    for (int gi = 0; gi < 2; ++gi) {
+      const int g = 2 * pp + gi;
+      if (g >= NG) break;
+      const uint32_t zc = (b.z[g] >> zshift) & 0xFu;
+      const h2 m1024 = __builtin_bit_cast(h2, (0xE400u | zc) * 0x00010001u);
+      const h2 m64 = __builtin_bit_cast(h2, (0xD400u | (zc << 4)) * 0x00010001u);
+      const half8 b0 = dequant_word(words[gi][0], bias, m1024, m64);
+      const half8 b1 = dequant_word(words[gi][1], bias, m1024, m64);
+      const float sf = half_bits_to_float(static_cast<uint16_t>(b.s[g]));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int nr = wave_nrow<GATE_UP>(wn, s) + j;
-      const uint32_t w = sm.bq[(gl * 4 + q) * kBStride + nr];
-      const uint32_t z = (sm.bz[gl * (kBN / 8) + (nr >> 3)] >> (4 * (nr & 7))) & 0xFu;
-      sc[s] = half_bits_to_float(sm.bs[gl * kBN + nr]);
-      const half8 b = exact_codes(w, z);
+      for (int i = 0; i < NS; ++i) {
+        const uint16_t* blk = stage + ((g * MSUB + i) * 2) * kBlockHalfs;
+        const int s0 = (lane ^ slot_xor(g, lane >> 5, 0)) * 8;
+        const int s1 = (lane ^ slot_xor(g, lane >> 5, 1)) * 8 + kBlockHalfs;
+        const half8 a0 = *reinterpret_cast<const half8*>(blk + s0);
+        const half8 a1 = *reinterpret_cast<const half8*>(blk + s1);
+        const float16v zero = {};
+        float16v pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, zero, 0, 0, 0);
+        pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, pr, 0, 0, 0);
+        if (!GATE_UP) {
+          const half8 l0 = *reinterpret_cast<const half8*>(blk + kLoOff + s0);
+          const half8 l1 = *reinterpret_cast<const half8*>(blk + kLoOff + s1);
+          pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(l0, b0, pr, 0, 0, 0);
+          pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(l1, b1, pr, 0, 0, 0);
+        }
+        if (g > 0 || i > 0) {
+          const int pi = i > 0 ? i - 1 : NS - 1;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const float4v zero = {0.f, 0.f, 0.f, 0.f};
-        p[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0][m], b, zero, 0, 0, 0);
-        if (!GATE_UP)
-          p[m][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[Stage<GATE_UP>::kARows - 1][m], b,
-                                                           p[m][s], 0, 0, 0);
+          for (int v = 0; v < 16; ++v) acc[pi][v] = fmaf(pend_s, pend[v], acc[pi][v]);
+        }
+        pend = pr;
+        pend_s = sf;
       }
     }
+  }
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+  for (int v = 0; v < 16; ++v) acc[NS - 1][v] = fmaf(pend_s, pend[v], acc[NS - 1][v]);
+}
+
+template <bool GATE_UP, int MSUB, int NS>
+__device__ __forceinline__ void main_loop(const ASrc& asrc, uint16_t* lds,
+                                          const BAddr& ba, uint32_t zshift,
+                                          float16v (&acc)[MSUB]) {
+  using S = AStage<GATE_UP, MSUB>;
+  constexpr int KC = S::kKC;
+  const int G = ba.G;
+  uint32_t bias;   // kept in a vector register so each mask-and-insert is one v_and_or_b32
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));
+  const int nfull = G / KC;
+  BRegs<KC> bcur, bnxt;
+  AStage<GATE_UP, MSUB> astage;
+  load_b_stage<KC>(ba, 0, bcur);
+  load_a<GATE_UP, MSUB, NS>(asrc, 0, astage);
+  store_a<GATE_UP, MSUB, NS>(astage, lds);
+  __syncthreads();
+  for (int s = 0; s < nfull; ++s) {
+    const int g0 = s * KC;
+    // The next stage's loads are issued unconditionally (past the end of K
+    // they read zeros or the following row), so every wait below is exact.
+    load_b_stage<KC>(ba, g0 + KC, bnxt);
+    load_a<GATE_UP, MSUB, NS>(asrc, g0 + KC, astage);
+    compute_stage<GATE_UP, MSUB, NS, KC>(lds + (s & 1) * S::kStageHalfs, bcur, zshift, bias, acc);
+    store_a<GATE_UP, MSUB, NS>(astage, lds + ((s + 1) & 1) * S::kStageHalfs);
+    bcur = bnxt;
+    __syncthreads();
+  }
+  // tail stage of G % KC groups, loaded by the last iteration
+  const int ng = G - nfull * KC;
+  const uint16_t* tail = lds + (nfull & 1) * S::kStageHalfs;
+  if (ng == 1) compute_stage<GATE_UP, MSUB, NS, 1>(tail, bcur, zshift, bias, acc);
+  if (KC > 2 && ng == 2) compute_stage<GATE_UP, MSUB, NS, (KC > 2 ? 2 : 1)>(tail, bcur, zshift, bias, acc);
+  if (KC > 3 && ng == 3) compute_stage<GATE_UP, MSUB, NS, (KC > 3 ? 3 : 1)>(tail, bcur, zshift, bias, acc);
+}
+
+template <bool GATE_UP, int MSUB>
+__global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n_ntiles) {
+  using S = AStage<GATE_UP, MSUB>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::kStageHalfs];
+
+  // Work item (M-tile, N-tile), M-tile-major; XCD x = blockIdx % 8 takes the
+  // x-th contiguous run of items.
+  const int total = *p.tile_count * n_ntiles;
+  const int per = (total + 7) >> 3;
+  const int run_idx = static_cast<int>(blockIdx.x >> 3);
+  if (run_idx >= per) return;
+  const int item = static_cast<int>(blockIdx.x & 7) * per + run_idx;
+  if (item >= total) return;
+  const int slot = item / n_ntiles;
+  const int nt = item - slot * n_ntiles;
+  const int e = p.tiles[2 * slot];
+  const int row0 = p.tiles[2 * slot + 1];
+  const int rows = min(S::kBM, p.offsets[e + 1] - row0);
+  const int nsub = (rows + kSub - 1) / kSub;
+  const int K = GATE_UP ? p.H : p.I;
+  const int N = GATE_UP ? 2 * p.I : p.H;
+  const int G = K / kGroup;
+
+  // A rows: stage 1 gathers x rows through the sorted slots; stage 2 reads
+  // the tile's own act rows (buffers based at the tile's first row).
+  ASrc asrc;
+  {
+    const int j = threadIdx.x / S::kTPR;
+    if (GATE_UP) {
+      const uint32_t bytes = static_cast<uint32_t>(p.T) * K * 2u;
+      asrc.r[0] = make_rsrc(p.a_hi, bytes);
+      asrc.r[1] = asrc.r[0];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int i = 0; i < MSUB; ++i) {
+        const int r = i * kSub + j;
+        asrc.row_off[i] = r < rows ? static_cast<uint32_t>(p.sorted_slots[row0 + r] / p.top_k) * K * 2u
+                                   : bytes;
+      }
+    } else {
+      const uint32_t bytes = static_cast<uint32_t>(rows) * K * 2u;
+      asrc.r[0] = make_rsrc(p.a_hi + static_cast<size_t>(row0) * K, bytes);
+      asrc.r[1] = make_rsrc(p.a_lo + static_cast<size_t>(row0) * K, bytes);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[m][s][v] = fmaf(sc[s], p[m][s][v], acc[m][s][v]);
+      for (int i = 0; i < MSUB; ++i) asrc.row_off[i] = static_cast<uint32_t>(i * kSub + j) * K * 2u;
+    }
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane & 31;
+  const int h = lane >> 5;
+  // This lane's weight row.  Stage 1: lanes 0..15 take gate columns c0..,
+  // lanes 16..31 the matching up columns.
+  int c0, n;
+  if (GATE_UP) {
+    c0 = nt * (kBN / 2) + wave * 16;
+    n = c0 < p.I ? (j < 16 ? c0 + j : p.I + c0 + j - 16) : N;
+  } else {
+    c0 = nt * kBN + wave * kSub;
+    n = c0 < N ? c0 + j : N;
+  }
+  const size_t wbase = static_cast<size_t>(e) * N;
+  const bool n_ok = n < N;
+  BAddr ba;
+  ba.G = G;
+  ba.h = h;
+  ba.rq = make_rsrc(p.qw + wbase * (G * 4), static_cast<uint32_t>(N) * G * 16u);
+  ba.rs = make_rsrc(p.sc + wbase * G, static_cast<uint32_t>(N) * G * 2u);
+  ba.rz = make_rsrc(p.qz + (wbase / 8) * G, static_cast<uint32_t>(N / 8) * G * 4u);
+  ba.q_oob = static_cast<uint32_t>(N) * G * 16u;
+  ba.s_oob = static_cast<uint32_t>(N) * G * 2u;
+  ba.z_oob = static_cast<uint32_t>(N / 8) * G * 4u;
+  // a lane past the matrix reads from the end of the buffers: zeros
+  ba.q_row = n_ok ? static_cast<uint32_t>(n) * G * 16u + h * 16u : ba.q_oob;
+  ba.s_row = n_ok ? static_cast<uint32_t>(n) * G * 2u : ba.s_oob;
+  ba.z_row = n_ok ? static_cast<uint32_t>(n >> 3) * G * 4u : ba.z_oob;
+  const uint32_t zshift = 4u * static_cast<uint32_t>(n & 7);
+
+  float16v acc[MSUB];
+#pragma unroll
+  for (int i = 0; i < MSUB; ++i) acc[i] = float16v{};
+
+  if (MSUB == 1 || nsub == 1)
+    main_loop<GATE_UP, MSUB, 1>(asrc, lds, ba, zshift, acc);
+  else if (nsub == 2)
+    main_loop<GATE_UP, MSUB, (MSUB >= 2 ? 2 : 1)>(asrc, lds, ba, zshift, acc);
+  else if (nsub == 3)
+    main_loop<GATE_UP, MSUB, (MSUB >= 3 ? 3 : 1)>(asrc, lds, ba, zshift, acc);
+  else
+    main_loop<GATE_UP, MSUB, MSUB>(asrc, lds, ba, zshift, acc);
+
+  // Epilogue: lane (h, j) holds rows 8 (v / 4) + 4 h + v % 4, column j of
+  // every 32 x 32 subtile.
+#pragma unroll
+  for (int i = 0; i < MSUB; ++i) {
+    if (i >= nsub) break;
+    if (GATE_UP) {
+      // Lanes j < 16 hold gate and lanes j + 16 the up value of the same
+      // column; each lane of the pair finishes 8 of the 16 rows.
+      const bool low = j < 16;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float send = low ? acc[i][u + 8] : acc[i][u];
+        const float recv = __shfl_xor(send, 16, 64);
+        const int v = low ? u : u + 8;
+        const float gate = low ? acc[i][u] : recv;
+        const float up = low ? recv : acc[i][u + 8];
+        const int r = i * kSub + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (r < rows && c0 < p.I) {
+          const float act = gate / (1.f + expf(-gate)) * up;
+          const uint16_t hi = float_to_half_bits(act);
+          const uint16_t lo = float_to_half_bits(act - half_bits_to_float(hi));
+          const size_t idx = static_cast<size_t>(row0 + r) * p.I + slot_pos(c0 + (j & 15));
+          p.act_hi[idx] = hi;
+          p.act_lo[idx] = lo;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = i * kSub + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (r < rows && n_ok) p.y[static_cast<size_t>(row0 + r) * p.H + n] = acc[i][v];
+      }
+    }
   }
 }
 
-// ------------------------------------------------------------------ kernels --
-// Tile list: for every active expert, ceil(rows / kBM) entries (expert, first
-// row); tile_count entries in total, in active-expert order.
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict__ offsets,
-                                                          const int* __restrict__ active,
-                                                          const int* __restrict__ num_active,
-                                                          int* __restrict__ tiles,
-                                                          int* __restrict__ tile_count) {
+// Block 0: the tile list.  For every active expert, ceil(rows / bm) entries
+// (expert, first row), in active-expert order; tile_count entries in total.
+// Blocks 1..: x permuted to k-slot order within every 8-wide block.
+__global__ __launch_bounds__(1024) void prefill_prep_kernel(
+    const int* __restrict__ offsets, const int* __restrict__ active,
+    const int* __restrict__ num_active, int bm, int* __restrict__ tiles,
+    int* __restrict__ tile_count, const uint16_t* __restrict__ x, uint16_t* __restrict__ xp,
+    int64_t chunks) {
+  if (blockIdx.x > 0) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x - 1) * 1024 + threadIdx.x;
+    if (c < chunks)
+      reinterpret_cast<uint4*>(xp)[c] = permute8(reinterpret_cast<const uint4*>(x)[c]);
+    return;
+  }
   __shared__ int wave_tot[17];
   constexpr int kPer = kMaxExperts / 1024;
   const int tid = threadIdx.x;
@@ -254,7 +479,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict
     cnt[i] = 0;
     if (a < na) {
       const int e = active[a];
-      cnt[i] = (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
+      cnt[i] = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
     }
     sum += cnt[i];
   }
@@ -289,7 +514,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict
       const int r0 = offsets[e];
       for (int t = 0; t < cnt[i]; ++t) {
         tiles[2 * (pos + t)] = e;
-        tiles[2 * (pos + t) + 1] = r0 + t * kBM;
+        tiles[2 * (pos + t) + 1] = r0 + t * bm;
       }
     }
     pos += cnt[i];
@@ -297,117 +522,59 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict
   if (tid == 0) *tile_count = wave_tot[16];
 }
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, FfnWorkspace ws,
-                                                            int n_ntiles) {
-  __shared__ Stage<GATE_UP> sm[2];
-  __shared__ int a_rows[kBM];
-  const int slot = blockIdx.x / n_ntiles;
-  const int nt = blockIdx.x - slot * n_ntiles;
-  if (slot >= *ws.tile_count) return;
-  const int e = ws.tiles[2 * slot];
-  const int row0 = ws.tiles[2 * slot + 1];
-  const int rows = min(kBM, p.offsets[e + 1] - row0);
-  const int K = GATE_UP ? p.H : p.I;
-  const int N = GATE_UP ? 2 * p.I : p.H;
-  const int G = K / kGroup;
-  const size_t wbase = static_cast<size_t>(e) * N;
-  const auto rq = make_rsrc(p.qw + wbase * (G * 4), static_cast<uint32_t>(N) * G * 16u);
-  const auto rs = make_rsrc(p.sc + wbase * G, static_cast<uint32_t>(N) * G * 2u);
-  const auto rz = make_rsrc(p.qz + (wbase / 8) * G, static_cast<uint32_t>(N / 8) * G * 4u);
+int tile_rows(int64_t S, int E) { return prefill_msub(S, E) * kSub; }
 
-  if (threadIdx.x < kBM) {
-    const int r = threadIdx.x;
-    int src = 0;
-    if (r < rows) src = GATE_UP ? p.sorted_slots[row0 + r] / p.top_k : row0 + r;
-    a_rows[r] = src;
-  }
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  float4v acc[2][4];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc[m][s] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  const int nstages = (G + kKC - 1) / kKC;
-  StageRegs st;
-  load_stage<GATE_UP>(p, ws.act_hi, ws.act_lo, a_rows, rows, K, N, G, 0, rq, rs, rz, nt, st);
-  store_stage<GATE_UP>(st, sm[0]);
-  __syncthreads();
-  for (int s = 0; s < nstages; ++s) {
-    const int g0 = s * kKC;
-    if (s + 1 < nstages)
-      load_stage<GATE_UP>(p, ws.act_hi, ws.act_lo, a_rows, rows, K, N, G, g0 + kKC, rq, rs, rz, nt, st);
-    compute_stage<GATE_UP>(sm[s & 1], min(kKC, G - g0), wm, wn, acc);
-    if (s + 1 < nstages) store_stage<GATE_UP>(st, sm[(s + 1) & 1]);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds rows 4 (lane / 16) + v and column lane % 16 of each subtile
-  const int lane = threadIdx.x & 63;
-  const int j = lane & 15;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = wm * 32 + m * 16 + (lane >> 4) * 4 + v;
-      if (r >= rows) continue;
-      if (GATE_UP) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int col = nt * (kBN / 2) + wn * 32 + s * 16 + j;
-          if (col < p.I) {
-            const float gate = acc[m][s][v];
-            const float up = acc[m][s + 2][v];
-            const float act = gate / (1.f + expf(-gate)) * up;
-            const uint16_t hi = float_to_half_bits(act);
-            const uint16_t lo = float_to_half_bits(act - half_bits_to_float(hi));
-            const size_t idx = static_cast<size_t>(row0 + r) * p.I + col;
-            ws.act_hi[idx] = hi;
-            ws.act_lo[idx] = lo;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int col = nt * kBN + wn * 64 + s * 16 + j;
-          if (col < p.H) p.y[static_cast<size_t>(row0 + r) * p.H + col] = acc[m][s][v];
-        }
-      }
-    }
-  }
+int64_t max_tiles(int64_t S, int E) {
+  const int bm = tile_rows(S, E);
+  return (S + bm - 1) / bm + std::min<int64_t>(E, S);
 }
 
-int max_tiles(int S, int E) { return (S + kBM - 1) / kBM + min(E, S); }
+unsigned grid_for(int64_t S, int E, int n_ntiles) {
+  const int64_t items = max_tiles(S, E) * n_ntiles;
+  return static_cast<unsigned>((items + 7) / 8 * 8);
+}
 
 }  // namespace
 
-void launch_build_tiles(const int* offsets, const int* active, const int* num_active,
-                        const FfnWorkspace& ws, hipStream_t stream) {
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, stream, offsets, active,
-                     num_active, ws.tiles, ws.tile_count);
+int prefill_msub(int64_t S, int E) { return S >= 64 * static_cast<int64_t>(E) ? 4 : 1; }
+
+void launch_prefill_prep(const uint16_t* x, int T, int H, const int* offsets, const int* active,
+                         const int* num_active, int64_t S, int E, const FfnWorkspace& ws,
+                         hipStream_t stream) {
+  const int64_t chunks = static_cast<int64_t>(T) * H / 8;
+  const unsigned blocks = 1 + static_cast<unsigned>((chunks + 1023) / 1024);
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3(blocks), dim3(1024), 0, stream, offsets, active,
+                     num_active, tile_rows(S, E), ws.tiles, ws.tile_count, x, ws.x_perm, chunks);
 }
 
 void launch_gate_up_prefill(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
-  PrefillArgs p{a.x, a.T, a.top_k, a.E, a.H, a.I, a.offsets, a.sorted_slots, a.qw, a.sc, a.qz,
-                nullptr};
+  PrefillArgs p{ws.x_perm, nullptr, a.sorted_slots, a.T, a.top_k, a.E, a.H, a.I, a.offsets,
+                ws.tiles, ws.tile_count, a.qw, a.sc, a.qz, ws.act_hi, ws.act_lo, nullptr};
+  const int64_t S = static_cast<int64_t>(a.T) * a.top_k;
   const int n_ntiles = (a.I + kBN / 2 - 1) / (kBN / 2);
-  const int slots = max_tiles(a.T * a.top_k, a.E);
-  hipLaunchKernelGGL((ffn_mfma_kernel<true>), dim3(static_cast<unsigned>(slots) * n_ntiles),
-                     dim3(kThreads), 0, stream, p, ws, n_ntiles);
+  const unsigned grid = grid_for(S, a.E, n_ntiles);
+  if (prefill_msub(S, a.E) == 4)
+    hipLaunchKernelGGL((ffn_mfma_kernel<true, 4>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       n_ntiles);
+  else
+    hipLaunchKernelGGL((ffn_mfma_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       n_ntiles);
 }
 
 void launch_down_prefill(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
-  PrefillArgs p{nullptr, a.T, a.top_k, a.E, a.H, a.I, a.offsets, nullptr, a.qw, a.sc, a.qz, a.y};
+  PrefillArgs p{ws.act_hi, ws.act_lo, nullptr, a.T, a.top_k, a.E, a.H, a.I, a.offsets,
+                ws.tiles, ws.tile_count, a.qw, a.sc, a.qz, nullptr, nullptr, a.y};
+  const int64_t S = static_cast<int64_t>(a.T) * a.top_k;
   const int n_ntiles = (a.H + kBN - 1) / kBN;
-  const int slots = max_tiles(a.T * a.top_k, a.E);
-  hipLaunchKernelGGL((ffn_mfma_kernel<false>), dim3(static_cast<unsigned>(slots) * n_ntiles),
-                     dim3(kThreads), 0, stream, p, ws, n_ntiles);
+  const unsigned grid = grid_for(S, a.E, n_ntiles);
+  if (prefill_msub(S, a.E) == 4)
+    hipLaunchKernelGGL((ffn_mfma_kernel<false, 4>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       n_ntiles);
+  else
+    hipLaunchKernelGGL((ffn_mfma_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       n_ntiles);
 }
 
-int prefill_max_tiles(int64_t S, int E) { return max_tiles(static_cast<int>(S), E); }
+int64_t prefill_max_tiles(int64_t S, int E) { return max_tiles(S, E); }
 
 }  // namespace moe
