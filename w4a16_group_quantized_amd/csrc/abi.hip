@@ -27,6 +27,16 @@ int check_routing(int64_t T, int32_t top_k, int32_t E) {
   return MOE_OK;
 }
 
+// The matrix-core variant addresses x with 32-bit byte offsets and numbers
+// its work items with int.
+int check_prefill(int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
+  if (T <= kDecodeMaxT) return MOE_OK;
+  if (T * static_cast<int64_t>(H) >= (static_cast<int64_t>(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (prefill_max_items(T * top_k, E, H, I) >= (static_cast<int64_t>(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 int check_dims(int32_t H, int32_t I, int32_t group_size) {
   if (group_size != kGroup) return MOE_ERR_UNSUPPORTED;
   if (H <= 0 || I <= 0 || H % kGroup || I % kGroup) return MOE_ERR_INVALID_ARG;
@@ -59,6 +69,7 @@ FfnWorkspace ffn_workspace_carve(void* base, int64_t T, int top_k, int E, int H,
   ws.act_lo = reinterpret_cast<uint16_t*>(p + act);
   ws.tiles = reinterpret_cast<int*>(p + 2 * act);
   ws.tile_count = reinterpret_cast<int*>(p + 2 * act + tiles);
+  ws.sched = ws.tile_count + 8;
   ws.x_perm = reinterpret_cast<uint16_t*>(p + 2 * act + tiles + 256);
   (void)H;
   return ws;
@@ -127,7 +138,7 @@ int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t
                       void* stream) {
   if (int st = check_routing(T, top_k, E)) return st;
   if (int st = check_dims(H, I, group_size)) return st;
-  if (T * static_cast<int64_t>(H) >= (static_cast<int64_t>(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (int st = check_prefill(T, top_k, E, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(expert_offsets) || !ok_ptr(sorted_slots) || !ok_ptr(active_experts) ||
       !ok_ptr(num_active) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) || !ok_ptr(w13_qzeros) ||
@@ -152,7 +163,7 @@ int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t
   if (T <= kDecodeMaxT) {
     launch_gate_up_decode(a, ws, static_cast<hipStream_t>(stream));
   } else {
-    launch_prefill_prep(x, static_cast<int>(T), H, expert_offsets, active_experts, num_active,
+    launch_prefill_prep(x, static_cast<int>(T), H, I, expert_offsets, active_experts, num_active,
                         T * top_k, E, ws, static_cast<hipStream_t>(stream));
     launch_gate_up_prefill(a, ws, static_cast<hipStream_t>(stream));
   }
@@ -166,6 +177,7 @@ int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
                    void* workspace, size_t workspace_bytes, void* stream) {
   if (int st = check_routing(T, top_k, E)) return st;
   if (int st = check_dims(H, I, group_size)) return st;
+  if (int st = check_prefill(T, top_k, E, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(expert_offsets) || !ok_ptr(active_experts) || !ok_ptr(num_active) ||
       !ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) || !ok_ptr(y_sorted) ||

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace moe {
 
 constexpr int kGroup = 32;          // quantisation group size along K
@@ -31,8 +33,10 @@ struct FfnWorkspace {
   uint16_t* act_lo;  // [S, I] fp16, act - act_hi rounded to fp16
   int* tiles;        // matrix-core M-tile list (prefill variant)
   int* tile_count;   // number of valid entries of `tiles`
+  int* sched;        // per GEMM (stride kSchedStride): bounds of its 8 work ranges
   uint16_t* x_perm;  // [T, H] x in k-slot order (prefill variant)
 };
+constexpr int kSchedStride = 16;    // ints per GEMM schedule (9 used)
 size_t ffn_workspace_bytes(int64_t T, int top_k, int E, int H, int I);
 FfnWorkspace ffn_workspace_carve(void* base, int64_t T, int top_k, int E, int H, int I);
 
@@ -65,16 +69,61 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
 // grouped GEMMs.  prefill_msub is the number of 32-row subtiles per M-tile
 // for S = T * top_k sorted rows over E experts.
 int prefill_msub(int64_t S, int E);
-int64_t prefill_max_tiles(int64_t S, int E);
-void launch_prefill_prep(const uint16_t* x, int T, int H, const int* offsets, const int* active,
-                         const int* num_active, int64_t S, int E, const FfnWorkspace& ws,
-                         hipStream_t stream);
+int64_t prefill_max_items(int64_t S, int E, int H, int I);   // grid of the larger GEMM
+void launch_prefill_prep(const uint16_t* x, int T, int H, int I, const int* offsets,
+                         const int* active, const int* num_active, int64_t S, int E,
+                         const FfnWorkspace& ws, hipStream_t stream);
 void launch_gate_up_prefill(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 void launch_down_prefill(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 
 void launch_combine(const float* y_sorted, const float* weights,
                     const int* slot_rows, int T, int top_k, int H,
                     uint16_t* out, hipStream_t stream);
+
+// ----------------------------------------------------------------------------
+// Host helper: workgroups of `kernel` (launched with `threads` threads and
+// `lds` bytes of dynamic LDS) that the current device holds at once.  The
+// occupancy query costs host time, so results are cached in `table` (one
+// table per kernel, kCacheSlots entries per device, each entry
+// (lds + 1) << 32 | workgroups).  A value never changes for a given device,
+// kernel and LDS size, so two threads racing on an entry store the same thing.
+// ----------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;   // devices with a cached occupancy figure
+constexpr int kCacheSlots = 8;
+using OccTable = std::atomic<uint64_t>[kMaxDevices * kCacheSlots];
+
+template <typename Kernel>
+int resident_workgroups(Kernel kernel, int threads, size_t lds, OccTable& table) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  const uint64_t key = static_cast<uint64_t>(lds + 1) << 32;
+  if (dev >= 0) {
+    for (int i = 0; i < kCacheSlots; ++i) {
+      const uint64_t v = table[dev * kCacheSlots + i].load(std::memory_order_relaxed);
+      if (v == 0) break;
+      if ((v & ~0xFFFFFFFFull) == key) return static_cast<int>(v & 0xFFFFFFFFull);
+    }
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess ||
+      cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int resident = per_cu * cus;
+  if (dev >= 0) {
+    for (int i = 0; i < kCacheSlots; ++i) {
+      uint64_t expected = 0;
+      std::atomic<uint64_t>& slot = table[dev * kCacheSlots + i];
+      if (slot.compare_exchange_strong(expected, key | static_cast<uint32_t>(resident)) ||
+          (expected & ~0xFFFFFFFFull) == key)
+        break;
+    }
+  }
+  return resident;
+}
 
 // ----------------------------------------------------------------------------
 // Device helpers

@@ -34,8 +34,6 @@
 // act at about 22 bits instead of fp16's 11.
 #include <math.h>
 
-#include <atomic>
-
 #include "common.h"
 
 namespace moe {
@@ -47,7 +45,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kDepth = 4;                 // weight loads in flight per lane (ring slots)
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for raw dword access on gfx9
 constexpr int kFragDwords = 20;           // LDS dwords per (A row, group): 16 pairs, c1, s, pad
-constexpr int kMaxDevices = 64;           // devices with a cached occupancy figure
 
 // ------------------------------------------------------------ A fragments ---
 // One A row's 32 values of a group, paired to match the nibble positions: for
@@ -401,47 +398,6 @@ int cluster_lanes(int G) {
   return C;
 }
 
-// Workgroups of `kernel` the device holds at once for a dynamic LDS size.
-// The occupancy query costs host time, so results are cached in `table`
-// (one table per kernel, kCacheSlots entries per device, each entry
-// (lds + 1) << 32 | workgroups).  A value never changes for a given device,
-// kernel and LDS size, so two threads racing on an entry store the same thing.
-constexpr int kCacheSlots = 8;
-using OccTable = std::atomic<uint64_t>[kMaxDevices * kCacheSlots];
-
-template <typename Kernel>
-int resident_workgroups(Kernel kernel, size_t lds, OccTable& table) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
-  const uint64_t key = static_cast<uint64_t>(lds + 1) << 32;
-  if (dev >= 0) {
-    for (int i = 0; i < kCacheSlots; ++i) {
-      const uint64_t v = table[dev * kCacheSlots + i].load(std::memory_order_relaxed);
-      if (v == 0) break;
-      if ((v & ~0xFFFFFFFFull) == key) return static_cast<int>(v & 0xFFFFFFFFull);
-    }
-  }
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
-          hipSuccess ||
-      cus < 1)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
-  const int resident = per_cu * cus;
-  if (dev >= 0) {
-    for (int i = 0; i < kCacheSlots; ++i) {
-      uint64_t expected = 0;
-      std::atomic<uint64_t>& slot = table[dev * kCacheSlots + i];
-      if (slot.compare_exchange_strong(expected, key | static_cast<uint32_t>(resident)) ||
-          (expected & ~0xFFFFFFFFull) == key)
-        break;
-    }
-  }
-  return resident;
-}
-
 // Spread each active-expert slot's blocks over as many waves as the chip
 // holds at once (no second round), each wave taking a contiguous run.
 void split_blocks(Geom& geo, int slots, int resident) {
@@ -456,7 +412,7 @@ void launch_gate_up_na(const GateUpArgs& a, const FfnWorkspace& ws, Geom geo, hi
   const size_t lds = static_cast<size_t>(NA) * geo.G * kFragDwords * sizeof(uint32_t);
   const int slots = min(a.E, a.T * a.top_k);
   static OccTable occ;
-  split_blocks(geo, slots, resident_workgroups(gate_up_decode_kernel<NA>, lds, occ));
+  split_blocks(geo, slots, resident_workgroups(gate_up_decode_kernel<NA>, kThreads, lds, occ));
   hipLaunchKernelGGL((gate_up_decode_kernel<NA>), dim3(static_cast<unsigned>(slots) * geo.splits),
                      dim3(kThreads), lds, stream, a, ws, geo);
 }
@@ -466,7 +422,7 @@ void launch_down_na(const DownArgs& a, const FfnWorkspace& ws, Geom geo, hipStre
   const size_t lds = static_cast<size_t>(2 * NA) * geo.G * kFragDwords * sizeof(uint32_t);
   const int slots = min(a.E, a.T * a.top_k);
   static OccTable occ;
-  split_blocks(geo, slots, resident_workgroups(down_decode_kernel<NA>, lds, occ));
+  split_blocks(geo, slots, resident_workgroups(down_decode_kernel<NA>, kThreads, lds, occ));
   hipLaunchKernelGGL((down_decode_kernel<NA>), dim3(static_cast<unsigned>(slots) * geo.splits),
                      dim3(kThreads), lds, stream, a, ws, geo);
 }

@@ -55,11 +55,16 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = kWaves * kSub;         // weight rows per N-tile
 constexpr int kBlockHalfs = 64 * 8;        // one fragment block: 64 lanes x 8 fp16
 constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3 for raw dword access on gfx9
+// Cost of a work item in 32-row subtiles: its live subtiles plus this base
+// (weight streaming and per-group vector work do not shrink with the rows).
+constexpr int kItemBase = 4;
 
-template <bool GATE_UP>
+// Groups per LDS stage: deeper for 32-row tiles, which stream weights with
+// little arithmetic per byte, so more bytes must be in flight per wave.
+template <bool GATE_UP, int MSUB>
 struct StageCfg {
   static constexpr int kCopies = GATE_UP ? 1 : 2;   // A copies: x, or act hi + lo
-  static constexpr int kKC = GATE_UP ? 4 : 2;       // groups per LDS stage
+  static constexpr int kKC = (GATE_UP ? 4 : 2) * (MSUB == 1 ? 2 : 1);
 };
 
 struct PrefillArgs {
@@ -171,8 +176,8 @@ __device__ __forceinline__ void load_b_stage(const BAddr& ba, int g0, BRegs<KC>&
 // past the end of the buffer (zeros, no traffic).
 template <bool GATE_UP, int MSUB>
 struct AStage {
-  static constexpr int kKC = StageCfg<GATE_UP>::kKC;
-  static constexpr int kCopies = StageCfg<GATE_UP>::kCopies;
+  static constexpr int kKC = StageCfg<GATE_UP, MSUB>::kKC;
+  static constexpr int kCopies = StageCfg<GATE_UP, MSUB>::kCopies;
   static constexpr int kBM = MSUB * kSub;
   static constexpr int kTPR = 8;                               // threads per row
   static constexpr int kCPR = kCopies * kKC * 4;               // chunks per row per stage
@@ -194,9 +199,9 @@ struct ASrc {
 __device__ __forceinline__ int slot_xor(int g, int h, int t) { return ((g & 1) << 2) | (h << 1) | t; }
 
 template <bool GATE_UP, int MSUB, int NS>
-__device__ __forceinline__ void load_a(const ASrc& src, int g0, AStage<GATE_UP, MSUB>& a) {
+__device__ __forceinline__ void load_a(uint32_t tid, const ASrc& src, int g0, AStage<GATE_UP, MSUB>& a) {
   using S = AStage<GATE_UP, MSUB>;
-  const int t8 = threadIdx.x % S::kTPR;
+  const int t8 = static_cast<int>(tid % S::kTPR);
   const int soff = g0 * kGroup * 2;
 #pragma unroll
   for (int i = 0; i < NS; ++i)
@@ -213,10 +218,10 @@ __device__ __forceinline__ void load_a(const ASrc& src, int g0, AStage<GATE_UP, 
 }
 
 template <bool GATE_UP, int MSUB, int NS>
-__device__ __forceinline__ void store_a(const AStage<GATE_UP, MSUB>& a, uint16_t* stage) {
+__device__ __forceinline__ void store_a(uint32_t tid, const AStage<GATE_UP, MSUB>& a, uint16_t* stage) {
   using S = AStage<GATE_UP, MSUB>;
-  const int j = threadIdx.x / S::kTPR;
-  const int t8 = threadIdx.x % S::kTPR;
+  const int j = static_cast<int>(tid / S::kTPR) & (kSub - 1);
+  const int t8 = static_cast<int>(tid % S::kTPR);
 #pragma unroll
   for (int i = 0; i < NS; ++i)
 #pragma unroll
@@ -235,13 +240,13 @@ __device__ __forceinline__ void store_a(const AStage<GATE_UP, MSUB>& a, uint16_t
 // tile with NS live 32-row subtiles.  The scaling of each partial is issued
 // after the next partial's MFMAs, so it does not wait on its own MFMA.
 template <bool GATE_UP, int MSUB, int NS, int NG>
-__device__ __forceinline__ void compute_stage(const uint16_t* stage,
-                                              const BRegs<StageCfg<GATE_UP>::kKC>& b,
+__device__ __forceinline__ void compute_stage(uint32_t tid, const uint16_t* stage,
+                                              const BRegs<StageCfg<GATE_UP, MSUB>::kKC>& b,
                                               uint32_t zshift, uint32_t bias,
                                               float16v (&acc)[MSUB]) {
-  constexpr int KC = StageCfg<GATE_UP>::kKC;
+  constexpr int KC = StageCfg<GATE_UP, MSUB>::kKC;
   constexpr int kLoOff = KC * MSUB * 2 * kBlockHalfs;   // act_lo copy
-  const int lane = threadIdx.x & 63;
+  const int lane = static_cast<int>(tid & 63);
   float16v pend = {};
   float pend_s = 0.f;
 #pragma unroll
@@ -291,8 +296,20 @@ __device__ __forceinline__ void compute_stage(const uint16_t* stage,
   for (int v = 0; v < 16; ++v) acc[NS - 1][v] = fmaf(pend_s, pend[v], acc[NS - 1][v]);
 }
 
+// Tail stage of NG < kKC groups, NG chosen at run time.
+template <bool GATE_UP, int MSUB, int NS, int NG>
+__device__ __forceinline__ void compute_tail(uint32_t tid, int ng, const uint16_t* stage,
+                                             const BRegs<StageCfg<GATE_UP, MSUB>::kKC>& b,
+                                             uint32_t zshift, uint32_t bias,
+                                             float16v (&acc)[MSUB]) {
+  if constexpr (NG >= 1) {
+    if (ng == NG) compute_stage<GATE_UP, MSUB, NS, NG>(tid, stage, b, zshift, bias, acc);
+    else compute_tail<GATE_UP, MSUB, NS, NG - 1>(tid, ng, stage, b, zshift, bias, acc);
+  }
+}
+
 template <bool GATE_UP, int MSUB, int NS>
-__device__ __forceinline__ void main_loop(const ASrc& asrc, uint16_t* lds,
+__device__ __forceinline__ void main_loop(uint32_t tid, const ASrc& asrc, uint16_t* lds,
                                           const BAddr& ba, uint32_t zshift,
                                           float16v (&acc)[MSUB]) {
   using S = AStage<GATE_UP, MSUB>;
@@ -304,43 +321,32 @@ __device__ __forceinline__ void main_loop(const ASrc& asrc, uint16_t* lds,
   BRegs<KC> bcur, bnxt;
   AStage<GATE_UP, MSUB> astage;
   load_b_stage<KC>(ba, 0, bcur);
-  load_a<GATE_UP, MSUB, NS>(asrc, 0, astage);
-  store_a<GATE_UP, MSUB, NS>(astage, lds);
+  load_a<GATE_UP, MSUB, NS>(tid, asrc, 0, astage);
+  store_a<GATE_UP, MSUB, NS>(tid, astage, lds);
   __syncthreads();
   for (int s = 0; s < nfull; ++s) {
     const int g0 = s * KC;
     // The next stage's loads are issued unconditionally (past the end of K
     // they read zeros or the following row), so every wait below is exact.
     load_b_stage<KC>(ba, g0 + KC, bnxt);
-    load_a<GATE_UP, MSUB, NS>(asrc, g0 + KC, astage);
-    compute_stage<GATE_UP, MSUB, NS, KC>(lds + (s & 1) * S::kStageHalfs, bcur, zshift, bias, acc);
-    store_a<GATE_UP, MSUB, NS>(astage, lds + ((s + 1) & 1) * S::kStageHalfs);
+    load_a<GATE_UP, MSUB, NS>(tid, asrc, g0 + KC, astage);
+    compute_stage<GATE_UP, MSUB, NS, KC>(tid, lds + (s & 1) * S::kStageHalfs, bcur, zshift, bias,
+                                         acc);
+    store_a<GATE_UP, MSUB, NS>(tid, astage, lds + ((s + 1) & 1) * S::kStageHalfs);
     bcur = bnxt;
     __syncthreads();
   }
   // tail stage of G % KC groups, loaded by the last iteration
-  const int ng = G - nfull * KC;
-  const uint16_t* tail = lds + (nfull & 1) * S::kStageHalfs;
-  if (ng == 1) compute_stage<GATE_UP, MSUB, NS, 1>(tail, bcur, zshift, bias, acc);
-  if (KC > 2 && ng == 2) compute_stage<GATE_UP, MSUB, NS, (KC > 2 ? 2 : 1)>(tail, bcur, zshift, bias, acc);
-  if (KC > 3 && ng == 3) compute_stage<GATE_UP, MSUB, NS, (KC > 3 ? 3 : 1)>(tail, bcur, zshift, bias, acc);
+  compute_tail<GATE_UP, MSUB, NS, KC - 1>(tid, G - nfull * KC, lds + (nfull & 1) * S::kStageHalfs,
+                                          bcur, zshift, bias, acc);
 }
 
+// One work item: M-tile `slot` of the tile list against N-tile `nt`.
 template <bool GATE_UP, int MSUB>
-__global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n_ntiles) {
+__device__ __forceinline__ void process_item(const PrefillArgs& p, int slot, int nt,
+                                             uint16_t* lds) {
   using S = AStage<GATE_UP, MSUB>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::kStageHalfs];
-
-  // Work item (M-tile, N-tile), M-tile-major; XCD x = blockIdx % 8 takes the
-  // x-th contiguous run of items.
-  const int total = *p.tile_count * n_ntiles;
-  const int per = (total + 7) >> 3;
-  const int run_idx = static_cast<int>(blockIdx.x >> 3);
-  if (run_idx >= per) return;
-  const int item = static_cast<int>(blockIdx.x & 7) * per + run_idx;
-  if (item >= total) return;
-  const int slot = item / n_ntiles;
-  const int nt = item - slot * n_ntiles;
+  const uint32_t tid = threadIdx.x;
   const int e = p.tiles[2 * slot];
   const int row0 = p.tiles[2 * slot + 1];
   const int rows = min(S::kBM, p.offsets[e + 1] - row0);
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n
   // the tile's own act rows (buffers based at the tile's first row).
   ASrc asrc;
   {
-    const int j = threadIdx.x / S::kTPR;
+    const int j = static_cast<int>(tid / S::kTPR) & (kSub - 1);
     if (GATE_UP) {
       const uint32_t bytes = static_cast<uint32_t>(p.T) * K * 2u;
       asrc.r[0] = make_rsrc(p.a_hi, bytes);
@@ -373,8 +379,8 @@ __global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n
     }
   }
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = static_cast<int>(tid & 63);
+  const int wave = static_cast<int>(tid >> 6) & (kWaves - 1);
   const int j = lane & 31;
   const int h = lane >> 5;
   // This lane's weight row.  Stage 1: lanes 0..15 take gate columns c0..,
@@ -409,13 +415,13 @@ __global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n
   for (int i = 0; i < MSUB; ++i) acc[i] = float16v{};
 
   if (MSUB == 1 || nsub == 1)
-    main_loop<GATE_UP, MSUB, 1>(asrc, lds, ba, zshift, acc);
+    main_loop<GATE_UP, MSUB, 1>(tid, asrc, lds, ba, zshift, acc);
   else if (nsub == 2)
-    main_loop<GATE_UP, MSUB, (MSUB >= 2 ? 2 : 1)>(asrc, lds, ba, zshift, acc);
+    main_loop<GATE_UP, MSUB, (MSUB >= 2 ? 2 : 1)>(tid, asrc, lds, ba, zshift, acc);
   else if (nsub == 3)
-    main_loop<GATE_UP, MSUB, (MSUB >= 3 ? 3 : 1)>(asrc, lds, ba, zshift, acc);
+    main_loop<GATE_UP, MSUB, (MSUB >= 3 ? 3 : 1)>(tid, asrc, lds, ba, zshift, acc);
   else
-    main_loop<GATE_UP, MSUB, MSUB>(asrc, lds, ba, zshift, acc);
+    main_loop<GATE_UP, MSUB, MSUB>(tid, asrc, lds, ba, zshift, acc);
 
   // Epilogue: lane (h, j) holds rows 8 (v / 4) + 4 h + v % 4, column j of
   // every 32 x 32 subtile.
@@ -453,73 +459,144 @@ __global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n
   }
 }
 
-// Block 0: the tile list.  For every active expert, ceil(rows / bm) entries
-// (expert, first row), in active-expert order; tile_count entries in total.
-// Blocks 1..: x permuted to k-slot order within every 8-wide block.
-__global__ __launch_bounds__(1024) void prefill_prep_kernel(
-    const int* __restrict__ offsets, const int* __restrict__ active,
-    const int* __restrict__ num_active, int bm, int* __restrict__ tiles,
-    int* __restrict__ tile_count, const uint16_t* __restrict__ x, uint16_t* __restrict__ xp,
-    int64_t chunks) {
-  if (blockIdx.x > 0) {
-    const int64_t c = static_cast<int64_t>(blockIdx.x - 1) * 1024 + threadIdx.x;
-    if (c < chunks)
-      reinterpret_cast<uint4*>(xp)[c] = permute8(reinterpret_cast<const uint4*>(x)[c]);
-    return;
-  }
-  __shared__ int wave_tot[17];
-  constexpr int kPer = kMaxExperts / 1024;
-  const int tid = threadIdx.x;
-  const int na = *num_active;
-  int cnt[kPer];
-  int sum = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int a = tid * kPer + i;
-    cnt[i] = 0;
-    if (a < na) {
-      const int e = active[a];
-      cnt[i] = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-    }
-    sum += cnt[i];
-  }
-  // block exclusive scan of `sum`
-  const int lane = tid & 63, wave = tid >> 6;
-  int inc = sum;
+// Work item i is (M-tile i / n_ntiles, N-tile i % n_ntiles).  The prep
+// kernel cut the items into 8 contiguous ranges of equal estimated cost;
+// workgroup b takes item b / 8 of range b % 8.  Workgroups are dealt to the
+// XCDs round-robin, so each XCD walks its own run of experts in order and the
+// workgroups running together share A rows and weights in their L2.  The grid
+// covers the longest possible range; workgroups past the end of their range
+// exit at once.
+template <bool GATE_UP, int MSUB>
+__global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n_ntiles,
+                                                            const int* __restrict__ sched) {
+  using S = AStage<GATE_UP, MSUB>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::kStageHalfs];
+  const int x = static_cast<int>(blockIdx.x & 7);
+  const int item = sched[x] + static_cast<int>(blockIdx.x >> 3);
+  if (item >= sched[x + 1]) return;
+  const int slot = item / n_ntiles;
+  process_item<GATE_UP, MSUB>(p, slot, item - slot * n_ntiles, lds);
+}
+
+// Exclusive scan over the 1024 threads of a block; returns the thread's
+// exclusive prefix and stores the total in tot[16].
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int o = __shfl_up(inc, d, 64);
     if (lane >= d) inc += o;
   }
-  if (lane == 63) wave_tot[wave] = inc;
+  if (lane == 63) tot[wave] = inc;
   __syncthreads();
   if (wave == 0) {
-    const int w = lane < 16 ? wave_tot[lane] : 0;
+    const int w = lane < 16 ? tot[lane] : 0;
     int winc = w;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int o = __shfl_up(winc, d, 64);
       if (lane >= d) winc += o;
     }
-    if (lane < 16) wave_tot[lane] = winc - w;
-    if (lane == 15) wave_tot[16] = winc;
+    if (lane < 16) tot[lane] = winc - w;
+    if (lane == 15) tot[16] = winc;
   }
   __syncthreads();
-  int pos = wave_tot[wave] + inc - sum;
+  const int r = tot[wave] + inc - v;
+  __syncthreads();   // tot is reused by the next scan
+  return r;
+}
+
+// Block 0: the tile list (for every active expert, ceil(rows / bm) entries
+// (expert, first row), in active-expert order), and for each of the two
+// GEMMs the bounds of its 8 work ranges.  Blocks 1..: x permuted to
+// k-slot order within every 8-wide block.
+__global__ __launch_bounds__(1024) void prefill_prep_kernel(
+    const int* __restrict__ offsets, const int* __restrict__ active,
+    const int* __restrict__ num_active, int bm, int base, int nn_gate_up, int nn_down,
+    int* __restrict__ tiles, int* __restrict__ tile_count, int* __restrict__ sched,
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int64_t chunks) {
+  if (blockIdx.x > 0) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x - 1) * 1024 + threadIdx.x;
+    if (c < chunks)
+      reinterpret_cast<uint4*>(xp)[c] = permute8(reinterpret_cast<const uint4*>(x)[c]);
+    return;
+  }
+  __shared__ int tot[17];
+  __shared__ int tile0[kMaxExperts + 1];   // per active expert: first tile
+  __shared__ int work0[kMaxExperts + 1];   // per active expert: subtiles before it
+  constexpr int kPer = kMaxExperts / 1024;
+  const int tid = threadIdx.x;
+  const int na = *num_active;
+  const int msub = bm / kSub;
+  int cnt[kPer], wk[kPer];
+  int csum = 0, wsum = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int a = tid * kPer + i;
+    cnt[i] = 0;
+    wk[i] = 0;
+    if (a < na) {
+      const int e = active[a];
+      const int rows = offsets[e + 1] - offsets[e];
+      cnt[i] = (rows + bm - 1) / bm;
+      wk[i] = (rows + kSub - 1) / kSub + base * cnt[i];
+    }
+    csum += cnt[i];
+    wsum += wk[i];
+  }
+  int pos = block_exclusive_scan(csum, tot);
+  const int total_tiles = tot[16];
+  __syncthreads();
+  int wpos = block_exclusive_scan(wsum, tot);
+  const int total_work = tot[16];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int a = tid * kPer + i;
     if (a < na) {
       const int e = active[a];
       const int r0 = offsets[e];
+      tile0[a] = pos;
+      work0[a] = wpos;
       for (int t = 0; t < cnt[i]; ++t) {
         tiles[2 * (pos + t)] = e;
         tiles[2 * (pos + t) + 1] = r0 + t * bm;
       }
     }
     pos += cnt[i];
+    wpos += wk[i];
   }
-  if (tid == 0) *tile_count = wave_tot[16];
+  if (tid == 0) {
+    *tile_count = total_tiles;
+    tile0[na] = total_tiles;
+    work0[na] = total_work;
+  }
+  __syncthreads();
+  if (tid < 16) {
+    // first item of range xr of GEMM k: the first item whose cumulative work
+    // reaches xr / 8 of the total
+    const int k = tid >> 3, xr = tid & 7;
+    const int nn = k ? nn_down : nn_gate_up;
+    int* sc = sched + k * kSchedStride;
+    const int64_t items = static_cast<int64_t>(total_tiles) * nn;
+    const int64_t target = static_cast<int64_t>(total_work) * nn * xr / 8;
+    int lo = 0, hi = na;   // last expert a with work0[a] * nn <= target
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (static_cast<int64_t>(work0[mid]) * nn <= target) lo = mid;
+      else hi = mid;
+    }
+    const int64_t r = target - static_cast<int64_t>(work0[lo]) * nn;
+    const int ntl = tile0[lo + 1] - tile0[lo];
+    const int wa = work0[lo + 1] - work0[lo];
+    const int wfull = msub + base;   // work of a full tile
+    const int u = static_cast<int>(min<int64_t>(r / (static_cast<int64_t>(wfull) * nn), ntl - 1));
+    const int w = min(wfull, wa - u * wfull);
+    const int64_t r2 = r - static_cast<int64_t>(u) * wfull * nn;
+    const int64_t first = static_cast<int64_t>(tile0[lo] + u) * nn + (r2 + w - 1) / w;
+    sc[xr] = static_cast<int>(min(first, items));
+    if (xr == 7) sc[8] = static_cast<int>(items);
+  }
 }
 
 int tile_rows(int64_t S, int E) { return prefill_msub(S, E) * kSub; }
@@ -529,52 +606,62 @@ int64_t max_tiles(int64_t S, int E) {
   return (S + bm - 1) / bm + std::min<int64_t>(E, S);
 }
 
-unsigned grid_for(int64_t S, int E, int n_ntiles) {
-  const int64_t items = max_tiles(S, E) * n_ntiles;
-  return static_cast<unsigned>((items + 7) / 8 * 8);
+// Workgroups per range.  An item of s live subtiles costs s + kItemBase, at
+// least 1 + kItemBase and at most (1 + kItemBase) s, so a range (1/8 of the
+// cost) holds at most 1/8 of the items' subtiles plus one item.  The subtiles
+// number at most one per 32 rows plus one per expert.
+int64_t range_bound(int64_t S, int E, int n_ntiles) {
+  const int64_t subtiles = (S + kSub - 1) / kSub + std::min<int64_t>(E, S);
+  return (subtiles * n_ntiles + 7) / 8 + 1;
 }
+
+template <bool GATE_UP, int MSUB>
+void launch_gemm(const PrefillArgs& p, int n_ntiles, const int* sched, hipStream_t stream) {
+  const int64_t per_range = range_bound(static_cast<int64_t>(p.T) * p.top_k, p.E, n_ntiles);
+  hipLaunchKernelGGL((ffn_mfma_kernel<GATE_UP, MSUB>), dim3(static_cast<unsigned>(8 * per_range)),
+                     dim3(kThreads), 0, stream, p, n_ntiles, sched);
+}
+
+int ntiles_gate_up(int I) { return (I + kBN / 2 - 1) / (kBN / 2); }
+int ntiles_down(int H) { return (H + kBN - 1) / kBN; }
 
 }  // namespace
 
 int prefill_msub(int64_t S, int E) { return S >= 64 * static_cast<int64_t>(E) ? 4 : 1; }
 
-void launch_prefill_prep(const uint16_t* x, int T, int H, const int* offsets, const int* active,
-                         const int* num_active, int64_t S, int E, const FfnWorkspace& ws,
-                         hipStream_t stream) {
+int64_t prefill_max_items(int64_t S, int E, int H, int I) {
+  return 8 * range_bound(S, E, std::max(ntiles_gate_up(I), ntiles_down(H)));
+}
+
+void launch_prefill_prep(const uint16_t* x, int T, int H, int I, const int* offsets,
+                         const int* active, const int* num_active, int64_t S, int E,
+                         const FfnWorkspace& ws, hipStream_t stream) {
   const int64_t chunks = static_cast<int64_t>(T) * H / 8;
   const unsigned blocks = 1 + static_cast<unsigned>((chunks + 1023) / 1024);
   hipLaunchKernelGGL(prefill_prep_kernel, dim3(blocks), dim3(1024), 0, stream, offsets, active,
-                     num_active, tile_rows(S, E), ws.tiles, ws.tile_count, x, ws.x_perm, chunks);
+                     num_active, tile_rows(S, E), kItemBase, ntiles_gate_up(I), ntiles_down(H), ws.tiles,
+                     ws.tile_count, ws.sched, x, ws.x_perm, chunks);
 }
 
 void launch_gate_up_prefill(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
   PrefillArgs p{ws.x_perm, nullptr, a.sorted_slots, a.T, a.top_k, a.E, a.H, a.I, a.offsets,
                 ws.tiles, ws.tile_count, a.qw, a.sc, a.qz, ws.act_hi, ws.act_lo, nullptr};
   const int64_t S = static_cast<int64_t>(a.T) * a.top_k;
-  const int n_ntiles = (a.I + kBN / 2 - 1) / (kBN / 2);
-  const unsigned grid = grid_for(S, a.E, n_ntiles);
   if (prefill_msub(S, a.E) == 4)
-    hipLaunchKernelGGL((ffn_mfma_kernel<true, 4>), dim3(grid), dim3(kThreads), 0, stream, p,
-                       n_ntiles);
+    launch_gemm<true, 4>(p, ntiles_gate_up(a.I), ws.sched, stream);
   else
-    hipLaunchKernelGGL((ffn_mfma_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, stream, p,
-                       n_ntiles);
+    launch_gemm<true, 1>(p, ntiles_gate_up(a.I), ws.sched, stream);
 }
 
 void launch_down_prefill(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
   PrefillArgs p{ws.act_hi, ws.act_lo, nullptr, a.T, a.top_k, a.E, a.H, a.I, a.offsets,
                 ws.tiles, ws.tile_count, a.qw, a.sc, a.qz, nullptr, nullptr, a.y};
   const int64_t S = static_cast<int64_t>(a.T) * a.top_k;
-  const int n_ntiles = (a.H + kBN - 1) / kBN;
-  const unsigned grid = grid_for(S, a.E, n_ntiles);
+  const int* sched = ws.sched + kSchedStride;
   if (prefill_msub(S, a.E) == 4)
-    hipLaunchKernelGGL((ffn_mfma_kernel<false, 4>), dim3(grid), dim3(kThreads), 0, stream, p,
-                       n_ntiles);
+    launch_gemm<false, 4>(p, ntiles_down(a.H), sched, stream);
   else
-    hipLaunchKernelGGL((ffn_mfma_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, stream, p,
-                       n_ntiles);
+    launch_gemm<false, 1>(p, ntiles_down(a.H), sched, stream);
 }
-
-int64_t prefill_max_tiles(int64_t S, int E) { return max_tiles(S, E); }
 
 }  // namespace moe
