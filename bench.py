@@ -100,17 +100,26 @@ def layer_work(shape, num_active: int) -> dict:
 # --------------------------------------------------------------------------- #
 # HBM traffic from rocprofv3 counters (committed summary, valid for one source)
 # --------------------------------------------------------------------------- #
-KERNEL_SOURCES = {
-    "gate_up": "w4a16_group_quantized_amd/csrc/ffn_decode.hip",
-    "down": "w4a16_group_quantized_amd/csrc/ffn_decode.hip",
-}
+DECODE_MAX_T = 8   # token counts at or below this run the GEMV kernels
 
 
-def source_sha256(rel: str) -> str:
+def kernel_sources(workload: str) -> list:
+    """Sources whose text fixes the FFN kernels a workload runs."""
+    from w4a16_group_quantized_amd.inputs import WORKLOADS
+
+    csrc = "w4a16_group_quantized_amd/csrc/"
+    main = "ffn_decode.hip" if WORKLOADS[workload].T <= DECODE_MAX_T else "ffn_prefill.hip"
+    return [csrc + main, csrc + "common.h"]
+
+
+def source_sha256(rels: list) -> str:
     import hashlib
 
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def counter_traffic(workload: str, kernel: str):
@@ -130,7 +139,7 @@ def counter_traffic(workload: str, kernel: str):
         if len(parts) < 2 or parts[0] != "traffic" or parts[1] != kernel:
             continue
         kv = dict(p.split("=", 1) for p in parts[2:])
-        if kv.get("source_sha256") != source_sha256(KERNEL_SOURCES[kernel]):
+        if kv.get("source_sha256") != source_sha256(kernel_sources(workload)):
             return None
         fetch = float(kv["fetch_kib"]) * float(kv["fetch_scale"]) * 1024
         write = float(kv["write_kib"]) * float(kv["write_scale"]) * 1024
