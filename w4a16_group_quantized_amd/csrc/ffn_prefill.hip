@@ -121,12 +121,14 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t bias, h2 m102
 }
 
 // Per-lane weight operands of one stage: codes of kKC / 2 group pairs (lane
-// half h loads group 2p + h of pair p), one zero word and one scale per group.
+// half h loads group 2p + h of pair p), one zero word per group and the
+// group scales packed two per dword.
 template <int KC>
 struct BRegs {
   uint4 q[KC / 2];
   uint32_t z[KC];
-  uint32_t s[KC];
+  uint32_t s[(KC + 1) / 2];
+  __device__ __forceinline__ uint32_t scale(int g) const { return (s[g >> 1] >> (16 * (g & 1))) & 0xFFFFu; }
 };
 
 struct BAddr {
@@ -137,36 +139,57 @@ struct BAddr {
   int h;                              // lane half
 };
 
-// Loads of one stage's weight operands.  FULL: every group of the stage lies
-// inside the matrix (offsets are the row base plus constants); otherwise
-// groups past the end read zeros.  Both forms issue the same loads in the same
-// order, so the wait counts after either agree.
-template <int KC, bool FULL>
-__device__ __forceinline__ void load_b(const BAddr& ba, int g0, BRegs<KC>& b) {
-  const uint32_t q0 = ba.q_row + static_cast<uint32_t>(g0) * 16u;
-  const uint32_t z0 = ba.z_row + static_cast<uint32_t>(g0) * 4u;
-  const uint32_t s0 = ba.s_row + static_cast<uint32_t>(g0) * 2u;
+// Loads of one stage's weight operands.  The lane's row is in the vector
+// offset and the group in the scalar offset, clamped to the matrix: a stage
+// past the end re-reads valid data that the compute skips, and a lane past
+// the matrix reads from the end of the buffers (zeros).  No branches and no
+// vector arithmetic, so the wait counts after the loads are exact.  VEC (the
+// group count is a multiple of kKC): a stage's zero words and scales of one
+// row are contiguous and aligned, and are read with one wide load each.
+template <int KC, bool VEC>
+__device__ __forceinline__ void load_b_stage(const BAddr& ba, int g0, BRegs<KC>& b) {
 #pragma unroll
   for (int pp = 0; pp < KC / 2; ++pp) {
     // lane half h loads group g0 + 2 pp + h: ba.q_row already holds h * 16
-    const uint32_t off = FULL || g0 + 2 * pp + ba.h < ba.G ? q0 + pp * 32u : ba.q_oob;
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rq, static_cast<int>(off), 0, 0);
+    const int g = min(g0 + 2 * pp, ba.G - 1);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rq, static_cast<int>(ba.q_row), g * 16, 0);
     b.q[pp] = make_uint4(v[0], v[1], v[2], v[3]);
   }
+  if constexpr (VEC) {
+    const int gs = min(g0, ba.G - KC);
+    const int zo = static_cast<int>(ba.z_row), so = static_cast<int>(ba.s_row);
+    if constexpr (KC == 2) {
+      const auto z = __builtin_amdgcn_raw_buffer_load_b64(ba.rz, zo, gs * 4, 0);
+      b.z[0] = z[0];
+      b.z[1] = z[1];
+    } else {
 #pragma unroll
-  for (int g = 0; g < KC; ++g) {
-    const bool live = FULL || g0 + g < ba.G;
-    const uint32_t zo = live ? z0 + g * 4u : ba.z_oob;
-    const uint32_t so = live ? s0 + g * 2u : ba.s_oob;
-    b.z[g] = __builtin_amdgcn_raw_buffer_load_b32(ba.rz, static_cast<int>(zo), 0, 0);
-    b.s[g] = __builtin_amdgcn_raw_buffer_load_b16(ba.rs, static_cast<int>(so), 0, 0);
+      for (int i = 0; i < KC; i += 4) {
+        const auto z = __builtin_amdgcn_raw_buffer_load_b128(ba.rz, zo, (gs + i) * 4, 0);
+        for (int t = 0; t < 4; ++t) b.z[i + t] = z[t];
+      }
+    }
+    if constexpr (KC == 8) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rs, so, gs * 2, 0);
+      for (int t = 0; t < 4; ++t) b.s[t] = v[t];
+    } else if constexpr (KC == 4) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ba.rs, so, gs * 2, 0);
+      b.s[0] = v[0];
+      b.s[1] = v[1];
+    } else {
+      b.s[0] = __builtin_amdgcn_raw_buffer_load_b32(ba.rs, so, gs * 2, 0);
+    }
+  } else {
+    uint32_t sv[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int g = min(g0 + i, ba.G - 1);
+      b.z[i] = __builtin_amdgcn_raw_buffer_load_b32(ba.rz, static_cast<int>(ba.z_row), g * 4, 0);
+      sv[i] = __builtin_amdgcn_raw_buffer_load_b16(ba.rs, static_cast<int>(ba.s_row), g * 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < KC; i += 2) b.s[i / 2] = sv[i] | (i + 1 < KC ? sv[i + 1] << 16 : 0u);
   }
-}
-
-template <int KC>
-__device__ __forceinline__ void load_b_stage(const BAddr& ba, int g0, BRegs<KC>& b) {
-  if (g0 + KC <= ba.G) load_b<KC, true>(ba, g0, b);
-  else load_b<KC, false>(ba, g0, b);
 }
 
 // A staging.  8 threads share a row, so each load instruction reads 128
@@ -265,7 +288,7 @@ __device__ __forceinline__ void compute_stage(uint32_t tid, const uint16_t* stag
       const h2 m64 = __builtin_bit_cast(h2, (0xD400u | (zc << 4)) * 0x00010001u);
       const half8 b0 = dequant_word(words[gi][0], bias, m1024, m64);
       const half8 b1 = dequant_word(words[gi][1], bias, m1024, m64);
-      const float sf = half_bits_to_float(static_cast<uint16_t>(b.s[g]));
+      const float sf = half_bits_to_float(static_cast<uint16_t>(b.scale(g)));
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const uint16_t* blk = stage + ((g * MSUB + i) * 2) * kBlockHalfs;
@@ -308,7 +331,7 @@ __device__ __forceinline__ void compute_tail(uint32_t tid, int ng, const uint16_
   }
 }
 
-template <bool GATE_UP, int MSUB, int NS>
+template <bool GATE_UP, int MSUB, int NS, bool VEC>
 __device__ __forceinline__ void main_loop(uint32_t tid, const ASrc& asrc, uint16_t* lds,
                                           const BAddr& ba, uint32_t zshift,
                                           float16v (&acc)[MSUB]) {
@@ -320,7 +343,7 @@ __device__ __forceinline__ void main_loop(uint32_t tid, const ASrc& asrc, uint16
   const int nfull = G / KC;
   BRegs<KC> bcur, bnxt;
   AStage<GATE_UP, MSUB> astage;
-  load_b_stage<KC>(ba, 0, bcur);
+  load_b_stage<KC, VEC>(ba, 0, bcur);
   load_a<GATE_UP, MSUB, NS>(tid, asrc, 0, astage);
   store_a<GATE_UP, MSUB, NS>(tid, astage, lds);
   __syncthreads();
@@ -328,10 +351,13 @@ __device__ __forceinline__ void main_loop(uint32_t tid, const ASrc& asrc, uint16
     const int g0 = s * KC;
     // The next stage's loads are issued unconditionally (past the end of K
     // they read zeros or the following row), so every wait below is exact.
-    load_b_stage<KC>(ba, g0 + KC, bnxt);
+    load_b_stage<KC, VEC>(ba, g0 + KC, bnxt);
     load_a<GATE_UP, MSUB, NS>(tid, asrc, g0 + KC, astage);
+    // keep the loads ahead of the compute that hides their latency
+    __builtin_amdgcn_sched_barrier(0);
     compute_stage<GATE_UP, MSUB, NS, KC>(tid, lds + (s & 1) * S::kStageHalfs, bcur, zshift, bias,
                                          acc);
+    __builtin_amdgcn_sched_barrier(0);
     store_a<GATE_UP, MSUB, NS>(tid, astage, lds + ((s + 1) & 1) * S::kStageHalfs);
     bcur = bnxt;
     __syncthreads();
@@ -342,7 +368,7 @@ __device__ __forceinline__ void main_loop(uint32_t tid, const ASrc& asrc, uint16
 }
 
 // One work item: M-tile `slot` of the tile list against N-tile `nt`.
-template <bool GATE_UP, int MSUB>
+template <bool GATE_UP, int MSUB, bool VEC>
 __device__ __forceinline__ void process_item(const PrefillArgs& p, int slot, int nt,
                                              uint16_t* lds) {
   using S = AStage<GATE_UP, MSUB>;
@@ -415,13 +441,13 @@ __device__ __forceinline__ void process_item(const PrefillArgs& p, int slot, int
   for (int i = 0; i < MSUB; ++i) acc[i] = float16v{};
 
   if (MSUB == 1 || nsub == 1)
-    main_loop<GATE_UP, MSUB, 1>(tid, asrc, lds, ba, zshift, acc);
+    main_loop<GATE_UP, MSUB, 1, VEC>(tid, asrc, lds, ba, zshift, acc);
   else if (nsub == 2)
-    main_loop<GATE_UP, MSUB, (MSUB >= 2 ? 2 : 1)>(tid, asrc, lds, ba, zshift, acc);
+    main_loop<GATE_UP, MSUB, (MSUB >= 2 ? 2 : 1), VEC>(tid, asrc, lds, ba, zshift, acc);
   else if (nsub == 3)
-    main_loop<GATE_UP, MSUB, (MSUB >= 3 ? 3 : 1)>(tid, asrc, lds, ba, zshift, acc);
+    main_loop<GATE_UP, MSUB, (MSUB >= 3 ? 3 : 1), VEC>(tid, asrc, lds, ba, zshift, acc);
   else
-    main_loop<GATE_UP, MSUB, MSUB>(tid, asrc, lds, ba, zshift, acc);
+    main_loop<GATE_UP, MSUB, MSUB, VEC>(tid, asrc, lds, ba, zshift, acc);
 
   // Epilogue: lane (h, j) holds rows 8 (v / 4) + 4 h + v % 4, column j of
   // every 32 x 32 subtile.
@@ -466,7 +492,7 @@ __device__ __forceinline__ void process_item(const PrefillArgs& p, int slot, int
 // workgroups running together share A rows and weights in their L2.  The grid
 // covers the longest possible range; workgroups past the end of their range
 // exit at once.
-template <bool GATE_UP, int MSUB>
+template <bool GATE_UP, int MSUB, bool VEC>
 __global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n_ntiles,
                                                             const int* __restrict__ sched) {
   using S = AStage<GATE_UP, MSUB>;
@@ -475,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n
   const int item = sched[x] + static_cast<int>(blockIdx.x >> 3);
   if (item >= sched[x + 1]) return;
   const int slot = item / n_ntiles;
-  process_item<GATE_UP, MSUB>(p, slot, item - slot * n_ntiles, lds);
+  process_item<GATE_UP, MSUB, VEC>(p, slot, item - slot * n_ntiles, lds);
 }
 
 // Exclusive scan over the 1024 threads of a block; returns the thread's
@@ -618,8 +644,14 @@ int64_t range_bound(int64_t S, int E, int n_ntiles) {
 template <bool GATE_UP, int MSUB>
 void launch_gemm(const PrefillArgs& p, int n_ntiles, const int* sched, hipStream_t stream) {
   const int64_t per_range = range_bound(static_cast<int64_t>(p.T) * p.top_k, p.E, n_ntiles);
-  hipLaunchKernelGGL((ffn_mfma_kernel<GATE_UP, MSUB>), dim3(static_cast<unsigned>(8 * per_range)),
-                     dim3(kThreads), 0, stream, p, n_ntiles, sched);
+  const dim3 grid(static_cast<unsigned>(8 * per_range));
+  const int G = (GATE_UP ? p.H : p.I) / kGroup;
+  if (G % StageCfg<GATE_UP, MSUB>::kKC == 0)
+    hipLaunchKernelGGL((ffn_mfma_kernel<GATE_UP, MSUB, true>), grid, dim3(kThreads), 0, stream, p,
+                       n_ntiles, sched);
+  else
+    hipLaunchKernelGGL((ffn_mfma_kernel<GATE_UP, MSUB, false>), grid, dim3(kThreads), 0, stream, p,
+                       n_ntiles, sched);
 }
 
 int ntiles_gate_up(int I) { return (I + kBN / 2 - 1) / (kBN / 2); }
