@@ -161,11 +161,17 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
     const int e = kPerThread * tid + i;
     int run = 0;
     if (e < E) {
-      for (int b = 0; b < nblocks; ++b) {
-        int* p = gcount + static_cast<size_t>(b) * E + e;
-        const int c = *p;
-        *p = run;
-        run += c;
+      // 16 block counts in flight at a time, then their exclusive prefixes
+      for (int b0 = 0; b0 < nblocks; b0 += 16) {
+        int c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          c[u] = b0 + u < nblocks ? gcount[static_cast<size_t>(b0 + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (b0 + u < nblocks) gcount[static_cast<size_t>(b0 + u) * E + e] = run;
+          run += c[u];
+        }
       }
     }
     cnt[i] = run;

@@ -1,16 +1,16 @@
 // Router: softmax over E expert logits, top-k, renormalised weights.
 //
-// One 64-lane wavefront per token.  Lane l holds logits l, l+64, ... in
-// registers; each of the top_k rounds takes every lane's best remaining logit
-// and reduces it across the wave with a butterfly on (value, index) pairs,
-// ordered by value descending and index ascending, so ties go to the lower
-// expert index and every lane ends the round with the same winner.  The
-// renormalised weights exp(l_j - l_0) / sum_j' exp(l_j' - l_0) equal the
-// renormalised softmax probabilities (the full-softmax denominator cancels).
-// Geometry source: the 512-expert top-10 routed experts of "[Model][SM70]
-// Adapt Qwen3.8 Flash Next NVFP4", section "Implemented route".
-#include <float.h>
-#include <limits.h>
+// One 64-lane wavefront per token.  Each logit becomes a 64-bit key: its
+// order-preserving bit pattern (with -0 folded onto +0) above the inverted
+// expert index, so the largest key is the largest logit and, among equal
+// logits, the lowest expert index.  Lane l holds the keys of experts l,
+// l + 64, ...; each of the top_k rounds takes the wave maximum of the lanes'
+// best keys (DPP within rows of 16 lanes, then v_permlane16/32_swap across
+// rows, all plain vector operations) and clears the winner.  The renormalised
+// weights exp(l_j - l_0) / sum_j' exp(l_j' - l_0) equal the renormalised
+// softmax probabilities (the full-softmax denominator cancels).  Geometry
+// source: the 512-expert top-10 routed experts of "[Model][SM70] Adapt
+// Qwen3.8 Flash Next NVFP4", section "Implemented route".
 #include <math.h>
 
 #include "common.h"
@@ -20,8 +20,52 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+__device__ __forceinline__ uint64_t logit_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;   // -0 ranks with +0
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(ord) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+}
+
+__device__ __forceinline__ float key_logit(uint64_t k) {
+  const uint32_t ord = static_cast<uint32_t>(k >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+__device__ __forceinline__ int key_expert(uint64_t k) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(k));
+}
+
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(x >> 32), CTRL, 0xF, 0xF, false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+// Maximum over the wave, returned in every lane.  The row swaps hand each lane
+// its partner 16 (32) lanes away in one of their two results, and the other
+// result is the lane's own value, so the maximum of all three is the pair's.
+__device__ __forceinline__ uint64_t wave_max(uint64_t k) {
+  k = max64(k, dpp64<0xB1>(k));    // quad_perm [1,0,3,2]
+  k = max64(k, dpp64<0x4E>(k));    // quad_perm [2,3,0,1]
+  k = max64(k, dpp64<0x141>(k));   // row_half_mirror
+  k = max64(k, dpp64<0x140>(k));   // row_mirror
+  {
+    const uint32_t lo = static_cast<uint32_t>(k), hi = static_cast<uint32_t>(k >> 32);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    k = max64(k, max64((static_cast<uint64_t>(h[0]) << 32) | l[0], (static_cast<uint64_t>(h[1]) << 32) | l[1]));
+  }
+  {
+    const uint32_t lo = static_cast<uint32_t>(k), hi = static_cast<uint32_t>(k >> 32);
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    k = max64(k, max64((static_cast<uint64_t>(h[0]) << 32) | l[0], (static_cast<uint64_t>(h[1]) << 32) | l[1]));
+  }
+  return k;
 }
 
 template <int NPL>  // logits per lane; E <= 64 * NPL
@@ -33,46 +77,30 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_topk_kernel(
   if (t >= T) return;  // uniform per wave
   const float* row = logits + static_cast<size_t>(t) * E;
 
-  float v[NPL];
-  uint64_t taken = 0;  // bit i set: element lane + 64 i is taken or absent
+  uint64_t key[NPL];  // 0: absent or taken (every real key is larger)
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    if (e < E) {
-      v[i] = row[e];
-    } else {
-      v[i] = -INFINITY;
-      taken |= 1ull << i;
-    }
+    key[i] = e < E ? logit_key(row[e], e) : 0ull;
   }
 
   float mine = 0.f;  // lane j keeps the logit chosen in round j
   float top = 0.f;   // logit of rank 0
   for (int j = 0; j < top_k; ++j) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + 64 * i;
-      if (!((taken >> i) & 1ull) && ranks_before(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
+    for (int i = 1; i < NPL; ++i) best = max64(best, key[i]);
+    best = wave_max(best);
+    const int e = key_expert(best);
+    const bool owner = (e & 63) == lane;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ranks_before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (bi != INT_MAX && (bi & 63) == lane) taken |= 1ull << (bi >> 6);
-    if (j == 0) top = bv;
+    for (int i = 0; i < NPL; ++i)
+      if (owner && i == (e >> 6)) key[i] = 0ull;
+    const float v = key_logit(best);
+    if (j == 0) top = v;
     if (lane == j) {
-      mine = bv;
-      ids[static_cast<size_t>(t) * top_k + j] = bi;
+      mine = v;
+      ids[static_cast<size_t>(t) * top_k + j] = e;
     }
   }
 
