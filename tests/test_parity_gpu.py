@@ -144,6 +144,9 @@ def test_token_counts(dev, T):
     (37, 5, 256, 96, 70),     # E not a multiple of 64, ragged I tile, > 64 tokens
     (100, 3, 96, 32, 17),     # small odd geometry
     (4096, 64, 64, 32, 3),    # largest E and top_k
+    (4, 2, 8192, 64, 4),      # decode, long K of gate/up: 32 steps per row block
+    (4, 2, 128, 4096, 3),     # decode, long K of down: 16 steps per row block
+    (6, 3, 96, 96, 2),        # decode, odd group counts: one lane per row
 ])
 def test_degenerate_shapes(dev, E, k, H, I, T):
     _full_check(synth.MoEShape(E=E, top_k=k, H=H, I=I, T=T), 5, dev)

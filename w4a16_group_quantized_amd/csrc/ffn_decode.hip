@@ -9,15 +9,25 @@
 // Work split.  A cluster of C lanes owns one weight row; lane c of the
 // cluster takes the row's quantisation groups c, c + C, ... (one 16-byte load
 // of codes per group), so each step of a wave reads C * 16 contiguous bytes
-// from each of its 64 / C rows.  A wave owns a contiguous run of row blocks of
-// one expert (stage 1: a block is R/2 gate rows in the lower half of the wave
-// and the matching R/2 up rows in the upper half, R = 64 / C), steps through
-// them with a ring of kDepth register slots of weight loads in flight, and
-// sums a row's groups within the cluster with DPP once the row is done;
-// nothing is synchronised across waves in the streaming loop.  The expert's
-// rows of A (x rows gathered through the sorted slots, or act rows) are staged
-// once per workgroup in LDS, already paired to the nibble layout, and read
-// back as broadcasts.  The grid is sized to what the chip holds at once.
+// from each of its 64 / C rows.  A block is the R = 64 / C rows a wave streams
+// together (stage 1: R/2 gate rows in the lower half of the wave and the
+// matching R/2 up rows in the upper half); a wave streams a block through a
+// ring of kDepth register slots of weight loads in flight and sums each row's
+// groups within its cluster with DPP when the block is done.  One workgroup
+// of 16 waves runs per compute unit; it owns an equal share of the
+// (expert, block) units and its waves take units from a counter in LDS, so
+// that all of them finish together (see the units section below).
+//
+// Staging.  Before streaming, a workgroup copies into LDS its experts' rows
+// of A (x rows gathered through the sorted slots, or act rows), already
+// paired to the nibble layout.  The fp16 scales of a unit (below) are loaded
+// with two 16-byte loads per lane by the wave that takes the unit, one unit
+// ahead, and written to that unit's slot in LDS.  Per step a lane then issues
+// one 16-byte code load and one 4-byte zero-word load to global memory; its
+// scale and A values come from LDS.  (Loading each 2-byte scale from global
+// memory in the step costs nearly as much in memory requests as the codes
+// themselves.)  The workgroup's barriers order LDS only, so the weight loads
+// issued before them stay in flight.
 //
 // Arithmetic.  A nibble q is turned into the fp16 number 1024 + q by OR-ing
 // it into the mantissa of 0x6400 (nibbles in bits 4..7 of a half give
@@ -40,7 +50,7 @@ namespace moe {
 namespace {
 
 constexpr uint32_t kOnes = 0x3C003C00u;   // fp16 1.0 in both halves
-constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kWaves = 16;                // waves per workgroup (one workgroup per compute unit)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDepth = 4;                 // weight loads in flight per lane (ring slots)
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for raw dword access on gfx9
@@ -50,8 +60,7 @@ constexpr int kFragDwords = 20;           // LDS dwords per (A row, group): 16 p
 // One A row's 32 values of a group, paired to match the nibble positions: for
 // 8-value block w, pairs (a0,a4), (a1,a5), (a2,a6), (a3,a7); plus
 // c1 = 1024 S_lo + 64 S_hi and s = S_lo + S_hi.  Written to LDS once.
-__device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ src, uint32_t* dst) {
-  const uint4* q = reinterpret_cast<const uint4*>(src);
+__device__ __forceinline__ void build_frag(const uint4 (&q)[4], uint32_t* dst) {
   uint32_t p[16];
   float slo = 0.f, shi = 0.f;
 #pragma unroll
@@ -72,6 +81,33 @@ __device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ src, uin
   *reinterpret_cast<uint2*>(dst + 16) =
       make_uint2(__builtin_bit_cast(uint32_t, 1024.f * slo + 64.f * shi),
                  __builtin_bit_cast(uint32_t, slo + shi));
+}
+
+__device__ __forceinline__ void load_group(const uint16_t* __restrict__ src, uint4 (&q)[4]) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) q[w] = s4[w];
+}
+
+__device__ __forceinline__ void stage_frag(const uint16_t* __restrict__ src, uint32_t* dst) {
+  uint4 q[4];
+  load_group(src, q);
+  build_frag(q, dst);
+}
+
+// A fragment as read back from LDS.
+struct Frag {
+  uint4 v[4];
+  uint2 c;
+};
+
+__device__ __forceinline__ Frag read_frag(const uint32_t* frag) {
+  const uint4* f4 = reinterpret_cast<const uint4*>(frag);
+  Frag f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) f.v[w] = f4[w];
+  f.c = *reinterpret_cast<const uint2*>(frag + 16);
+  return f;
 }
 
 // Nibble codes of one group as biased fp16 pairs (see the file comment).
@@ -99,60 +135,30 @@ __device__ __forceinline__ Codes expand_codes(const uint4 qv) {
   return k;
 }
 
-// sum_k (q_k - z) a_k over one group, A fragment read from LDS.
-__device__ __forceinline__ float group_dot(const Codes& k, float z, const uint32_t* frag) {
-  const uint4* f4 = reinterpret_cast<const uint4*>(frag);
+// sum_k (q_k - z) a_k over one group.
+__device__ __forceinline__ float group_dot(const Codes& k, float z, const Frag& f) {
   float ta = 0.f, tb = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const uint4 f = f4[w];
-    ta = dot2_f16(k.a[w], f.x, ta);
-    tb = dot2_f16(k.b[w], f.y, tb);
-    ta = dot2_f16(k.c[w], f.z, ta);
-    tb = dot2_f16(k.d[w], f.w, tb);
+    ta = dot2_f16(k.a[w], f.v[w].x, ta);
+    tb = dot2_f16(k.b[w], f.v[w].y, tb);
+    ta = dot2_f16(k.c[w], f.v[w].z, ta);
+    tb = dot2_f16(k.d[w], f.v[w].w, tb);
   }
-  const uint2 cs = *reinterpret_cast<const uint2*>(frag + 16);
-  return fmaf(-z, __builtin_bit_cast(float, cs.y),
-              fmaf(tb, 0.0625f, ta) - __builtin_bit_cast(float, cs.x));
+  return fmaf(-z, __builtin_bit_cast(float, f.c.y),
+              fmaf(tb, 0.0625f, ta) - __builtin_bit_cast(float, f.c.x));
 }
 
 // ------------------------------------------------------------ weight ring ---
-// One step's loads, kept exactly as loaded until the step is computed.
+// One step's global loads, kept exactly as loaded until the step is computed.
 struct Slot {
   uint4 q;
-  uint32_t s;
   uint32_t zw;
-};
-
-struct ExpertBufs {
-  __amdgpu_buffer_rsrc_t q, s, z;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
                                            kBufferFlags);
-}
-
-// Raw buffer loads take a 32-bit offset against a uniform base and return 0
-// past the end without touching memory, so a row index of `rows` is a free
-// "no load".
-__device__ __forceinline__ ExpertBufs expert_bufs(const int* qw, const uint16_t* sc, const int* qz,
-                                                  int rows, int G) {
-  ExpertBufs b;
-  b.q = make_rsrc(qw, static_cast<uint32_t>(rows) * G * 16u);
-  b.s = make_rsrc(sc, static_cast<uint32_t>(rows) * G * 2u);
-  b.z = make_rsrc(qz, static_cast<uint32_t>(rows / 8) * G * 4u);
-  return b;
-}
-
-__device__ __forceinline__ void load_slot(const ExpertBufs& b, int G, uint32_t row, uint32_t g,
-                                          Slot& s) {
-  const uint32_t idx = __umul24(row, G) + g;
-  const auto qv = __builtin_amdgcn_raw_buffer_load_b128(b.q, static_cast<int>(idx * 16u), 0, 0);
-  s.q = make_uint4(qv[0], qv[1], qv[2], qv[3]);
-  s.s = __builtin_amdgcn_raw_buffer_load_b16(b.s, static_cast<int>(idx * 2u), 0, 0);
-  s.zw = __builtin_amdgcn_raw_buffer_load_b32(
-      b.z, static_cast<int>((__umul24(row >> 3, G) + g) * 4u), 0, 0);
 }
 
 template <int CTRL>
@@ -171,18 +177,64 @@ __device__ __forceinline__ float cluster_sum(float v, int C) {
   return v;
 }
 
-// Geometry of one stage, fixed per launch.
+// ----------------------------------------------------------------- units ---
+// Work is cut into units (active-expert slot a, block b), numbered a * nb + b.
+// Workgroup w of nwg owns the units [U w / nwg, U (w + 1) / nwg), U =
+// num_active * nb, and works through them in windows of at most kXE experts
+// and wmax units.  For a window it stages in LDS the A rows of its experts
+// (na rows per expert per pass; more passes when an expert has more rows),
+// then its 16 waves take units from an LDS counter until the window is done
+// (the first unit of wave i is unit w0 + i, primed before staging), each
+// wave bringing its unit's scales into the unit's LDS slot.  Taking units
+// dynamically matters: waves that share a SIMD are served oldest first, so
+// equal static shares finish far apart in time.
 struct Geom {
-  int G;       // groups along K
-  int C;       // lanes per row (cluster); rows per wave block R = 64 / C
-  int spb;     // steps per block = ceil(G / C)
-  int nb;      // blocks per expert
-  int bpw;     // blocks per wave
-  int splits;  // workgroups per active-expert slot
+  int G;     // groups along K
+  int C;     // lanes per row (cluster); rows per block R = 64 / C
+  int spb;   // steps per block = G / C
+  int nb;    // blocks per expert
+  int nwg;   // workgroups (one per compute unit)
+  int wmax;  // units per window (bounded by LDS)
 };
 
-// Weight row that lane cluster k reads in block b, or `rows` when there is
-// none.  Stage 1: lower half of the wave gate rows, upper half up rows.
+constexpr int kXE = 2;  // experts per window
+
+// Workgroup barrier that orders LDS accesses only.  (__syncthreads also
+// waits for every global load in flight, here the weight loads issued ahead
+// of the barrier on purpose.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Element i (0 or 1) of a two-entry per-window table, without indexing a
+// private array by a run-time value.
+__device__ __forceinline__ int pick(const int (&t)[kXE], int i) { return i == 0 ? t[0] : t[1]; }
+
+struct DecodeArgs {
+  const uint16_t* x;       // stage 1 A: x [T, H]
+  const uint16_t* a_hi;    // stage 2 A: act_hi, act_lo [S, I]
+  const uint16_t* a_lo;
+  const int* offsets;
+  const int* sorted_slots;
+  const int* active;
+  const int* num_active;
+  const int* qw;
+  const uint16_t* sc;
+  const int* qz;
+  int T, top_k, H, I;
+  uint16_t* act_hi;        // stage 1 outputs
+  uint16_t* act_lo;
+  float* y;                // stage 2 output
+};
+
+// Scale halves of one unit: the R rows of its block (stage 1: R/2 gate rows,
+// then R/2 up rows), G each; R * G = 64 * spb.
+__device__ __host__ __forceinline__ int unit_scale_halves(int spb) { return 64 * spb; }
+
+// Weight row that lane cluster k streams in block b, or `rows_w` when there
+// is none.  Stage 1: lower half of the wave gate rows, upper half up rows.
 template <bool GATE_UP>
 __device__ __forceinline__ int block_row(int b, int k, int R, int I, int H) {
   if (GATE_UP) {
@@ -195,198 +247,285 @@ __device__ __forceinline__ int block_row(int b, int k, int R, int I, int H) {
   return n < H ? n : H;
 }
 
-// ------------------------------------------------------------------ kernel --
-// Per-wave step geometry of one run of blocks [b0, b1).
-struct WaveRun {
-  int k, lc, R, S, b0;
+// Scales of a unit, as staged in LDS: its R rows x G halves (stage 1: R/2
+// gate rows, then R/2 up rows), 8 spb chunks of 16 bytes.  A unit's rows are
+// one (stage 2) or two (stage 1) contiguous ranges of 32 spb halves, 16-byte
+// aligned, so chunk i is one 16-byte load; its byte offset into the
+// expert's scale array follows (a ragged last block reads past the end and
+// gets zeros from the buffer load).
+template <bool GATE_UP>
+__device__ __forceinline__ uint32_t scale_chunk(int I, int G, int spb, int R, int b, int i) {
+  const int x = i * 8;  // halves into the unit's block
+  int row0, xr;
+  if (GATE_UP) {
+    const bool up = x >= 32 * spb;
+    xr = up ? x - 32 * spb : x;
+    row0 = (up ? I : 0) + b * (R >> 1);
+  } else {
+    xr = x;
+    row0 = b * R;
+  }
+  return (static_cast<uint32_t>(row0) * G + xr) * 2u;
+}
+
+constexpr int kMaxSpbHeld = 16;  // units of up to 128 chunks are carried in two loads per lane
+
+// Buffer descriptors of expert e's weights.  Raw buffer loads take a 32-bit
+// offset against a uniform base and return 0 past the end without touching
+// memory, so a row index of rows_w is a free "no load".
+struct ExpertBufs {
+  __amdgpu_buffer_rsrc_t q, z, s;
 };
 
-__device__ __forceinline__ WaveRun wave_run(const Geom& geo, int b0, int b1) {
-  const int lane = threadIdx.x & 63;
-  WaveRun w;
-  w.R = 64 / geo.C;
-  w.k = lane / geo.C;
-  w.lc = lane & (geo.C - 1);
-  w.S = (b1 - b0) * geo.spb;
-  w.b0 = b0;
-  return w;
+__device__ __forceinline__ ExpertBufs expert_bufs(const DecodeArgs& p, int rows_w, int G, int e) {
+  ExpertBufs b;
+  b.q = make_rsrc(p.qw + static_cast<size_t>(e) * rows_w * (G * 4),
+                  static_cast<uint32_t>(rows_w) * G * 16u);
+  b.z = make_rsrc(p.qz + static_cast<size_t>(e) * (rows_w / 8) * G,
+                  static_cast<uint32_t>(rows_w / 8) * G * 4u);
+  b.s = make_rsrc(p.sc + static_cast<size_t>(e) * rows_w * G, static_cast<uint32_t>(rows_w) * G * 2u);
+  return b;
 }
 
-// Issue the loads of step s into a slot (a no-load when s is past the run).
-template <bool GATE_UP>
-__device__ __forceinline__ void load_step(const ExpertBufs& bufs, const Geom& geo, const WaveRun& w,
-                                          int rows_w, int I, int H, int s, Slot& slot) {
-  const int gg = (s % geo.spb) * geo.C + w.lc;
-  const bool live = s < w.S && gg < geo.G;
-  const uint32_t row = live ? block_row<GATE_UP>(w.b0 + s / geo.spb, w.k, w.R, I, H) : rows_w;
-  load_slot(bufs, geo.G, row, live ? gg : 0, slot);
+__device__ __forceinline__ void issue_step(const ExpertBufs& bufs, int G, uint32_t row, int gg,
+                                           Slot& sl) {
+  const uint32_t idx = row * static_cast<uint32_t>(G) + gg;
+  const auto qv = __builtin_amdgcn_raw_buffer_load_b128(bufs.q, static_cast<int>(idx * 16u), 0, 0);
+  sl.q = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+  sl.zw = __builtin_amdgcn_raw_buffer_load_b32(
+      bufs.z, static_cast<int>(((row >> 3) * static_cast<uint32_t>(G) + gg) * 4u), 0, 0);
 }
 
-// Fill the ring with the first kDepth steps.  Needs only the expert, so it
-// is issued before the A rows are staged.
-template <bool GATE_UP>
-__device__ __forceinline__ void prime_ring(const ExpertBufs& bufs, const Geom& geo,
-                                           const WaveRun& w, int rows_w, int I, int H,
-                                           Slot (&ring)[kDepth]) {
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d) load_step<GATE_UP>(bufs, geo, w, rows_w, I, H, d, ring[d]);
+__device__ __forceinline__ uint4 load_b128(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Streams the wave's run of blocks for mc (<= NA) rows of A, the ring already
-// primed.  Stage 2 fragments come in (hi, lo) pairs: fragment 2m is act_hi of
-// row m, 2m + 1 its act_lo.
+// Rows of A that the window's expert i holds in pass c, and where its
+// fragments sit in LDS.
+struct WinExpert {
+  int e, r0, rows;
+};
+
 template <bool GATE_UP, int NA>
-__device__ __forceinline__ void stream_expert(const ExpertBufs& bufs, const Geom& geo,
-                                              const WaveRun& wr, Slot (&ring)[kDepth], int rows_w,
-                                              int I, int H, const uint32_t* frags, int mc,
-                                              int r_first, uint16_t* act_hi, uint16_t* act_lo,
-                                              float* y) {
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo) {
+  // 16-byte aligned: fragments and scales are read with 16-byte LDS loads,
+  // and the static counter below would otherwise shift the dynamic area
+  extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ int queue;
+  constexpr int FPR = GATE_UP ? 1 : 2;        // fragments per A row (stage 2: hi, lo)
+  constexpr int NF = NA * FPR;                // fragments per expert and pass
+  const int G = geo.G, C = geo.C, spb = geo.spb, nb = geo.nb;
+  const int I = p.I, H = p.H;
+  const int rows_w = GATE_UP ? 2 * I : H;
+  const int R = 64 / C, half = R >> 1;
   const int lane = threadIdx.x & 63;
-  const int C = geo.C;
-  const int R = wr.R;
-  const int k = wr.k;
-  const int lc = wr.lc;
-  const int G = geo.G;
-  const int spb = geo.spb;
-  const int S = wr.S;
-  const int b0 = wr.b0;
+  // the wave index is the same in every lane; saying so keeps the unit
+  // bookkeeping in scalar registers and its branches uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k = lane / C, lc = lane & (C - 1);
+  uint32_t* frags = lds;
+  uint16_t* scales = reinterpret_cast<uint16_t*>(lds + kXE * NF * G * kFragDwords);
 
-  constexpr int NF = GATE_UP ? NA : 2 * NA;  // fragments per chunk of A rows
-  const int nf = GATE_UP ? mc : 2 * mc;
-  float acc[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = 0.f;
+  const int n_active = *p.num_active;
+  const int64_t U = static_cast<int64_t>(n_active) * nb;
+  const int u0 = static_cast<int>(U * blockIdx.x / geo.nwg);
+  const int u1 = static_cast<int>(U * (blockIdx.x + 1) / geo.nwg);
 
-  for (int s0 = 0; s0 < S; s0 += kDepth) {
+  for (int w0 = u0; w0 < u1;) {
+    const int a0 = w0 / nb;
+    const int w1 = min(u1, min(w0 + geo.wmax, (a0 + kXE) * nb));
+    const int nx = (w1 - 1) / nb - a0 + 1;
+    // the window's experts; their row counts are read once the weight loads
+    // of the first pass are out (that pass needs none: every active expert
+    // has a row)
+    int xe[kXE], xr0[kXE] = {0, 0}, xrows[kXE] = {1, 1};
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int s = s0 + d;
-      if (s < S) {
-        const int b = b0 + s / spb;
-        const int j = s - (s / spb) * spb;
-        const int gg = j * C + lc;
-        const uint32_t row = static_cast<uint32_t>(block_row<GATE_UP>(b, k, R, I, H));
-        const Slot& sl = ring[d];
-        const float scale = half_bits_to_float(static_cast<uint16_t>(sl.s));
-        const float z = static_cast<float>((sl.zw >> (4u * (row & 7u))) & 0xFu);
-        const Codes codes = expand_codes(sl.q);
-        const uint32_t* fr = frags + (gg < G ? gg : 0) * kFragDwords;
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-          if (f < nf) acc[f] = fmaf(scale, group_dot(codes, z, fr + f * G * kFragDwords), acc[f]);
-        if (j == spb - 1) {  // block done: finish its rows
-#pragma unroll
-          for (int m = 0; m < NA; ++m) {
-            if (m < mc) {
-              if (GATE_UP) {
-                const float v = cluster_sum(acc[m], C);
-                const float u = __shfl_xor(v, 32, 64);  // up half of the wave -> gate half
-                const int col = b * (R >> 1) + k;
-                if (lane < 32 && lc == 0 && col < I) {
-                  const float act = v / (1.f + expf(-v)) * u;
-                  const uint16_t hi = float_to_half_bits(act);
-                  const uint16_t lo = float_to_half_bits(act - half_bits_to_float(hi));
-                  const size_t idx = static_cast<size_t>(r_first + m) * I + col;
-                  act_hi[idx] = hi;
-                  act_lo[idx] = lo;
-                }
-              } else {
-                const float v = cluster_sum(acc[2 * m] + acc[2 * m + 1], C);
-                const int n = b * R + k;
-                if (lc == 0 && n < H) y[static_cast<size_t>(r_first + m) * H + n] = v;
-              }
-            }
+    for (int i = 0; i < kXE; ++i) xe[i] = i < nx ? p.active[a0 + i] : 0;
+    int maxrows = 1;
+    for (int c = 0; c < maxrows; c += NA) {
+      if (w0 != u0 || c != 0) lds_barrier();  // the previous pass no longer reads LDS
+      auto has_rows = [&](int u) { return c == 0 || pick(xrows, u / nb - a0) > c; };
+      auto take = [&]() -> int {  // next unit from the window's counter, or -1
+        int u;
+        do {
+          int t = 0;
+          if (lane == 0) t = atomicAdd(&queue, 1);
+          u = __builtin_amdgcn_readfirstlane(t);
+        } while (u < w1 && !has_rows(u));
+        return u < w1 ? u : -1;
+      };
+      // ---- load side.  lu is the unit being loaded, -2 when the next one is
+      // still to be taken from the counter, -1 when the window is done.  The
+      // ring is primed with the wave's first unit (unit w0 + wave) before
+      // staging; the counter is only used once staging is over.
+      Slot ring[kDepth];
+      int su[kDepth], sj[kDepth];  // unit (-1: none) and step of each ring slot
+      int lu = (w0 + wave < w1 && has_rows(w0 + wave)) ? w0 + wave : -2;
+      int lj = 0;
+      ExpertBufs lbufs = expert_bufs(p, rows_w, G, xe[0]);
+      uint32_t lrow = rows_w;
+      // A unit's scales are loaded when the load side enters it (held in sc0,
+      // sc1) and written to the unit's LDS slot when the compute side starts
+      // it; with the registers still holding a unit not yet written, the load
+      // side waits (only when a unit has fewer steps than the ring has slots).
+      // Units with more than kMaxSpbHeld steps are copied synchronously by
+      // the compute side instead.
+      const int nch = 8 * spb;
+      const bool held = spb <= kMaxSpbHeld;
+      uint4 sc0 = make_uint4(0, 0, 0, 0), sc1 = sc0;
+      bool pending = false;
+      auto issue = [&](int d, bool may_take) {
+        if (lu == -2 && may_take) lu = take();
+        const bool on = lu >= 0 && !(lj == 0 && pending);
+        if (on && lj == 0) {  // entering unit lu
+          const int a = lu / nb;
+          const int b = lu - a * nb;
+          lbufs = expert_bufs(p, rows_w, G, pick(xe, a - a0));
+          lrow = static_cast<uint32_t>(block_row<GATE_UP>(b, k, R, I, H));
+          if (held) {
+            sc0 = load_b128(lbufs.s, scale_chunk<GATE_UP>(I, G, spb, R, b, min(lane, nch - 1)));
+            sc1 = load_b128(lbufs.s, scale_chunk<GATE_UP>(I, G, spb, R, b, min(lane + 64, nch - 1)));
+            pending = true;
           }
+        }
+        issue_step(lbufs, G, on ? lrow : rows_w, lj * C + lc, ring[d]);
+        su[d] = on ? lu : -1;
+        sj[d] = lj;
+        if (on && ++lj == spb) {
+          lj = 0;
+          lu = -2;
+        }
+      };
 #pragma unroll
-          for (int f = 0; f < NF; ++f) acc[f] = 0.f;
+      for (int d = 0; d < kDepth; ++d) issue(d, false);
+
+      if (c == 0) {
+#pragma unroll
+        for (int i = 0; i < kXE; ++i) {
+          xr0[i] = i < nx ? p.offsets[xe[i]] : 0;
+          xrows[i] = i < nx ? p.offsets[xe[i] + 1] - xr0[i] : 0;
+          maxrows = max(maxrows, xrows[i]);
         }
       }
-      // Refill this slot with the step kDepth ahead; past the end this is a
-      // no-load, issued anyway so every path keeps the same wait counts.
-      load_step<GATE_UP>(bufs, geo, wr, rows_w, I, H, s + kDepth, ring[d]);
-    }
-  }
-}
+      // this pass's A rows
+      for (int i = threadIdx.x; i < kXE * NF * G; i += kThreads) {
+        const int xi = i / (NF * G);
+        const int rem = i - xi * (NF * G);
+        const int f = rem / G;
+        const int g = rem - f * G;
+        const int m = c + f / FPR;
+        if (xi < nx && m < pick(xrows, xi)) {
+          const int r = pick(xr0, xi) + m;
+          const uint16_t* src;
+          if (GATE_UP) {
+            src = p.x + static_cast<size_t>(p.sorted_slots[r] / p.top_k) * H;
+          } else {
+            src = ((f & 1) ? p.a_lo : p.a_hi) + static_cast<size_t>(r) * I;
+          }
+          stage_frag(src + 32 * g, frags + i * kFragDwords);
+        }
+      }
+      if (threadIdx.x == 0) queue = w0 + kWaves;
+      lds_barrier();
 
-template <int NA>
-__global__ __launch_bounds__(kThreads) void gate_up_decode_kernel(GateUpArgs args, FfnWorkspace ws,
-                                                                  Geom geo) {
-  extern __shared__ uint32_t frags[];
-  const int a_idx = blockIdx.x / geo.splits;
-  const int split = blockIdx.x - a_idx * geo.splits;
-  const int n_active = *args.num_active;
-  const int e = args.active[a_idx];  // in bounds: a_idx < min(E, T * top_k)
-  if (a_idx >= n_active) return;
-  const int I = args.I, H = args.H, G = geo.G;
-  const int wave_id = split * kWaves + (threadIdx.x >> 6);
-  const int b0 = min(geo.nb, wave_id * geo.bpw);
-  const int b1 = min(geo.nb, b0 + geo.bpw);
-  const size_t rows_w = static_cast<size_t>(2 * I);
-  const ExpertBufs bufs = expert_bufs(args.qw + static_cast<size_t>(e) * rows_w * (G * 4),
-                                      args.sc + static_cast<size_t>(e) * rows_w * G,
-                                      args.qz + static_cast<size_t>(e) * (rows_w / 8) * G,
-                                      2 * I, G);
-  const WaveRun wr = wave_run(geo, b0, b1);
-  Slot ring[kDepth];
-  prime_ring<true>(bufs, geo, wr, 2 * I, I, H, ring);
-  const int r0 = args.offsets[e];
-  const int rows_e = args.offsets[e + 1] - r0;
-  for (int m0 = 0; m0 < rows_e; m0 += NA) {
-    const int mc = min(NA, rows_e - m0);
-    if (m0 > 0) {
-      __syncthreads();  // previous chunk's fragments are no longer read
-      prime_ring<true>(bufs, geo, wr, 2 * I, I, H, ring);
+      // compute side
+      float acc[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[f] = 0.f;
+      int cmc = 0, crf = 0, cscale = 0;
+      int fb[NA];  // LDS dword offset of each A row's first fragment
+#pragma unroll
+      for (int m = 0; m < NA; ++m) fb[m] = 0;
+      uint32_t crow = 0;
+      int cb = 0;
+      bool live = true;
+      while (live) {
+        live = lu != -1;
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          if (su[d] >= 0) {
+            live = true;
+            const int j = sj[d];
+            if (j == 0) {  // a new unit: its expert, block and staged data
+              const int u = su[d];
+              const int a = u / nb;
+              const int xi = a - a0;
+              cb = u - a * nb;
+              crow = static_cast<uint32_t>(block_row<GATE_UP>(cb, k, R, I, H));
+              cmc = min(NA, pick(xrows, xi) - c);
+              crf = pick(xr0, xi) + c;
+#pragma unroll
+              for (int m = 0; m < NA; ++m) fb[m] = (xi * NF + m * FPR) * G * kFragDwords;
+              uint4* slot4 = reinterpret_cast<uint4*>(scales + (u - w0) * unit_scale_halves(spb));
+              if (held) {  // chunks lane and lane + 64 (repeats of the last one past the end)
+                slot4[min(lane, nch - 1)] = sc0;
+                slot4[min(lane + 64, nch - 1)] = sc1;
+                pending = false;
+              } else {
+                const ExpertBufs cb_bufs = expert_bufs(p, rows_w, G, pick(xe, xi));
+                for (int i = lane; i < nch; i += 64)
+                  slot4[i] = load_b128(cb_bufs.s, scale_chunk<GATE_UP>(I, G, spb, R, cb, i));
+              }
+              cscale = (u - w0) * unit_scale_halves(spb) +
+                       (GATE_UP ? (k < half ? 0 : 32 * spb) + (k < half ? k : k - half) * G : k * G);
+            }
+            const int gg = j * C + lc;
+            // LDS reads first: they do not wait for the weight loads.  Every
+            // chunk has at least one A row, so row 0's fragments are in use.
+            Frag fp[FPR];
+#pragma unroll
+            for (int f = 0; f < FPR; ++f) fp[f] = read_frag(frags + fb[0] + (f * G + gg) * kFragDwords);
+            const float scale = half_bits_to_float(scales[cscale + gg]);
+            __builtin_amdgcn_sched_barrier(0);
+            const Slot& sl = ring[d];
+            const float z = static_cast<float>((sl.zw >> (4u * (crow & 7u))) & 0xFu);
+            const Codes codes = expand_codes(sl.q);
+#pragma unroll
+            for (int f = 0; f < FPR; ++f) acc[f] = fmaf(scale, group_dot(codes, z, fp[f]), acc[f]);
+#pragma unroll
+            for (int m = 1; m < NA; ++m)
+              if (m < cmc) {
+#pragma unroll
+                for (int f = 0; f < FPR; ++f)
+                  acc[m * FPR + f] =
+                      fmaf(scale, group_dot(codes, z, read_frag(frags + fb[m] + (f * G + gg) * kFragDwords)),
+                           acc[m * FPR + f]);
+              }
+            if (j == spb - 1) {  // block done: finish its rows
+#pragma unroll
+              for (int m = 0; m < NA; ++m) {
+                if (m < cmc) {
+                  if (GATE_UP) {
+                    const float v = cluster_sum(acc[m], C);
+                    const float up = __shfl_xor(v, 32, 64);  // up half of the wave -> gate half
+                    const int col = cb * half + k;
+                    if (lane < 32 && lc == 0 && col < I) {
+                      const float act = v / (1.f + expf(-v)) * up;
+                      const uint16_t hi = float_to_half_bits(act);
+                      const uint16_t lo = float_to_half_bits(act - half_bits_to_float(hi));
+                      const size_t idx = static_cast<size_t>(crf + m) * I + col;
+                      p.act_hi[idx] = hi;
+                      p.act_lo[idx] = lo;
+                    }
+                  } else {
+                    const float v = cluster_sum(acc[2 * m] + acc[2 * m + 1], C);
+                    const int n = cb * R + k;
+                    if (lc == 0 && n < H) p.y[static_cast<size_t>(crf + m) * H + n] = v;
+                  }
+                }
+              }
+#pragma unroll
+              for (int f = 0; f < NF; ++f) acc[f] = 0.f;
+            }
+          }
+          // Refill this slot with the next step; once the window is done this
+          // is a no-load, issued anyway so every path keeps the same counts.
+          issue(d, true);
+        }
+      }
     }
-    for (int i = threadIdx.x; i < mc * G; i += kThreads) {
-      const int m = i / G;
-      const int g = i - m * G;
-      const int token = args.sorted_slots[r0 + m0 + m] / args.top_k;
-      stage_frag(args.x + static_cast<size_t>(token) * H + 32 * g, frags + i * kFragDwords);
-    }
-    __syncthreads();
-    stream_expert<true, NA>(bufs, geo, wr, ring, 2 * I, I, H, frags, mc, r0 + m0, ws.act_hi,
-                            ws.act_lo, nullptr);
-  }
-}
-
-template <int NA>
-__global__ __launch_bounds__(kThreads) void down_decode_kernel(DownArgs args, FfnWorkspace ws,
-                                                               Geom geo) {
-  extern __shared__ uint32_t frags[];
-  const int a_idx = blockIdx.x / geo.splits;
-  const int split = blockIdx.x - a_idx * geo.splits;
-  const int n_active = *args.num_active;
-  const int e = args.active[a_idx];
-  if (a_idx >= n_active) return;
-  const int I = args.I, H = args.H, G = geo.G;
-  const int wave_id = split * kWaves + (threadIdx.x >> 6);
-  const int b0 = min(geo.nb, wave_id * geo.bpw);
-  const int b1 = min(geo.nb, b0 + geo.bpw);
-  const size_t rows_w = static_cast<size_t>(H);
-  const ExpertBufs bufs = expert_bufs(args.qw + static_cast<size_t>(e) * rows_w * (G * 4),
-                                      args.sc + static_cast<size_t>(e) * rows_w * G,
-                                      args.qz + static_cast<size_t>(e) * (rows_w / 8) * G, H, G);
-  const WaveRun wr = wave_run(geo, b0, b1);
-  Slot ring[kDepth];
-  prime_ring<false>(bufs, geo, wr, H, I, H, ring);
-  const int r0 = args.offsets[e];
-  const int rows_e = args.offsets[e + 1] - r0;
-  for (int m0 = 0; m0 < rows_e; m0 += NA) {
-    const int mc = min(NA, rows_e - m0);
-    if (m0 > 0) {
-      __syncthreads();
-      prime_ring<false>(bufs, geo, wr, H, I, H, ring);
-    }
-    // fragment f = 2 m + {0: hi, 1: lo} of act row r0 + m0 + m, at f * G + g
-    for (int i = threadIdx.x; i < 2 * mc * G; i += kThreads) {
-      const int f = i / G;
-      const int g = i - f * G;
-      const size_t off = static_cast<size_t>(r0 + m0 + (f >> 1)) * I + 32 * g;
-      stage_frag(((f & 1) ? ws.act_lo : ws.act_hi) + off, frags + i * kFragDwords);
-    }
-    __syncthreads();
-    stream_expert<false, NA>(bufs, geo, wr, ring, H, I, H, frags, mc, r0 + m0, nullptr, nullptr,
-                             args.y);
+    w0 = w1;
   }
 }
 
@@ -398,60 +537,125 @@ int cluster_lanes(int G) {
   return C;
 }
 
-// Spread each active-expert slot's blocks over as many waves as the chip
-// holds at once (no second round), each wave taking a contiguous run.
-void split_blocks(Geom& geo, int slots, int resident) {
-  int splits = max(1, resident / max(1, slots));
-  splits = min(splits, (geo.nb + kWaves - 1) / kWaves);
-  geo.bpw = (geo.nb + splits * kWaves - 1) / (splits * kWaves);
-  geo.splits = (geo.nb + geo.bpw * kWaves - 1) / (geo.bpw * kWaves);
+struct DeviceInfo {
+  int cus;
+  int lds;
+};
+
+DeviceInfo device_info() {
+  static std::atomic<uint64_t> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const uint64_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v) return {static_cast<int>(v >> 32), static_cast<int>(v & 0xFFFFFFFFu)};
+  }
+  int cus = 0, lds = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess ||
+      cus < 1)
+    cus = 256;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev < 0 ? 0 : dev) !=
+          hipSuccess ||
+      lds < 65536)
+    lds = 65536;
+  if (dev >= 0)
+    cache[dev].store((static_cast<uint64_t>(cus) << 32) | static_cast<uint32_t>(lds),
+                     std::memory_order_relaxed);
+  return {cus, lds};
 }
 
-template <int NA>
-void launch_gate_up_na(const GateUpArgs& a, const FfnWorkspace& ws, Geom geo, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(NA) * geo.G * kFragDwords * sizeof(uint32_t);
-  const int slots = min(a.E, a.T * a.top_k);
-  static OccTable occ;
-  split_blocks(geo, slots, resident_workgroups(gate_up_decode_kernel<NA>, kThreads, lds, occ));
-  hipLaunchKernelGGL((gate_up_decode_kernel<NA>), dim3(static_cast<unsigned>(slots) * geo.splits),
-                     dim3(kThreads), lds, stream, a, ws, geo);
+// LDS bytes of the A fragments: kXE experts x na rows (stage 2: hi and lo).
+template <bool GATE_UP>
+size_t frag_bytes(const Geom& geo, int na) {
+  return static_cast<size_t>(kXE) * na * (GATE_UP ? 1 : 2) * geo.G * kFragDwords * 4;
 }
 
-template <int NA>
-void launch_down_na(const DownArgs& a, const FfnWorkspace& ws, Geom geo, hipStream_t stream) {
-  const size_t lds = static_cast<size_t>(2 * NA) * geo.G * kFragDwords * sizeof(uint32_t);
-  const int slots = min(a.E, a.T * a.top_k);
-  static OccTable occ;
-  split_blocks(geo, slots, resident_workgroups(down_decode_kernel<NA>, kThreads, lds, occ));
-  hipLaunchKernelGGL((down_decode_kernel<NA>), dim3(static_cast<unsigned>(slots) * geo.splits),
-                     dim3(kThreads), lds, stream, a, ws, geo);
+// Rows per expert per pass (a template value of the kernel) and the window
+// size, from the LDS a workgroup may hold.  Windows aim to cover a
+// workgroup's whole share of units, which is at most ceil(slots * nb / nwg).
+template <bool GATE_UP>
+int plan(Geom& geo, int T, int slots, const DeviceInfo& dev) {
+  const size_t budget = static_cast<size_t>(dev.lds) - 256;
+  const size_t unit = static_cast<size_t>(unit_scale_halves(geo.spb)) * 2;
+  const int want = static_cast<int>((static_cast<int64_t>(slots) * geo.nb + geo.nwg - 1) / geo.nwg) + 1;
+  int na = T >= 2 ? 2 : 1;
+  while (na > 1 && frag_bytes<GATE_UP>(geo, na) + unit * min(want, 16) > budget) na /= 2;
+  const size_t fb = frag_bytes<GATE_UP>(geo, na);
+  const size_t rest = budget > fb ? budget - fb : 0;
+  size_t w = rest / unit;
+  if (w > static_cast<size_t>(want)) w = want;
+  geo.wmax = w < 1 ? 1 : static_cast<int>(w);
+  return na;
+}
+
+template <bool GATE_UP>
+size_t launch_lds(const Geom& geo, int na) {
+  return frag_bytes<GATE_UP>(geo, na) +
+         static_cast<size_t>(geo.wmax) * unit_scale_halves(geo.spb) * 2;
+}
+
+template <bool GATE_UP>
+void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream) {
+  const DeviceInfo dev = device_info();
+  geo.nwg = dev.cus;
+  const int na = plan<GATE_UP>(geo, p.T, slots, dev);
+  const size_t lds = launch_lds<GATE_UP>(geo, na);
+  const dim3 grid(static_cast<unsigned>(geo.nwg)), block(kThreads);
+  if (na == 2)
+    hipLaunchKernelGGL((decode_kernel<GATE_UP, 2>), grid, block, lds, stream, p, geo);
+  else
+    hipLaunchKernelGGL((decode_kernel<GATE_UP, 1>), grid, block, lds, stream, p, geo);
 }
 
 }  // namespace
 
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
-  Geom geo;
+  Geom geo{};
   geo.G = a.H / kGroup;
   geo.C = cluster_lanes(geo.G);
-  geo.spb = (geo.G + geo.C - 1) / geo.C;
+  geo.spb = geo.G / geo.C;
   const int half = (64 / geo.C) / 2;  // gate (= up) rows per block
   geo.nb = (a.I + half - 1) / half;
-  if (a.T == 1)
-    launch_gate_up_na<1>(a, ws, geo, stream);
-  else
-    launch_gate_up_na<2>(a, ws, geo, stream);
+  DecodeArgs p{};
+  p.x = a.x;
+  p.offsets = a.offsets;
+  p.sorted_slots = a.sorted_slots;
+  p.active = a.active;
+  p.num_active = a.num_active;
+  p.qw = a.qw;
+  p.sc = a.sc;
+  p.qz = a.qz;
+  p.T = a.T;
+  p.top_k = a.top_k;
+  p.H = a.H;
+  p.I = a.I;
+  p.act_hi = ws.act_hi;
+  p.act_lo = ws.act_lo;
+  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream);
 }
 
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
-  Geom geo;
+  Geom geo{};
   geo.G = a.I / kGroup;
   geo.C = cluster_lanes(geo.G);
-  geo.spb = (geo.G + geo.C - 1) / geo.C;
+  geo.spb = geo.G / geo.C;
   geo.nb = (a.H + 64 / geo.C - 1) / (64 / geo.C);
-  if (a.T == 1)
-    launch_down_na<1>(a, ws, geo, stream);
-  else
-    launch_down_na<2>(a, ws, geo, stream);
+  DecodeArgs p{};
+  p.a_hi = ws.act_hi;
+  p.a_lo = ws.act_lo;
+  p.offsets = a.offsets;
+  p.active = a.active;
+  p.num_active = a.num_active;
+  p.qw = a.qw;
+  p.sc = a.sc;
+  p.qz = a.qz;
+  p.T = a.T;
+  p.top_k = a.top_k;
+  p.H = a.H;
+  p.I = a.I;
+  p.y = a.y;
+  launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream);
 }
 
 }  // namespace moe
