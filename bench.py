@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert W4A16 group-32 MoE layer on one MI355X.
 
-A step is one whole layer call (moe_route, moe_permute, moe_w4a16_grouped_ffn,
-moe_combine) over one batch of seeded synthetic input with every input already
-resident in HBM.  The default workload is the 512-expert, top-10,
+A step is one whole layer call (moe_route_permute, i.e. the router and the
+permutation, then moe_w4a16_grouped_ffn and moe_combine) over one batch of
+seeded synthetic input with every input already resident in HBM.  The default workload is the 512-expert, top-10,
 hidden-2560, intermediate-640 layer at 8 decode tokens.
 
 Measurement
@@ -230,8 +230,8 @@ def main(argv=None) -> int:
         w = copies[i % args.layers]
         if ev is not None:
             ev[0].record(stream)
-        ops.moe_route(logits, shape.top_k, layer.ids, layer.weights)
-        ops.moe_permute(layer.ids, shape.E, layer.perm_ws, layer.perm)
+        ops.moe_route_permute(logits, shape.top_k, layer.perm_ws, layer.ids, layer.weights,
+                              layer.perm)
         if ev is not None:
             ev[1].record(stream)
         ops.moe_w4a16_gate_up(x, shape.top_k, layer.perm, w, layer.ffn_ws)

@@ -125,6 +125,31 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
                 int32_t* num_active, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/*
+ * moe_route_permute - moe_route followed by moe_permute, in one call: the
+ * outputs of both, bit for bit identical to calling them in turn (routing of
+ * "[Model][SM70] Adapt Qwen3.8 Flash Next NVFP4", section "Implemented route";
+ * segments and offsets of "[Perf][SM70] Narrow Qwen3.8 AWQ active grouped
+ * decode", section "Purpose").  For T <= 64 and E <= 1024 it is one kernel
+ * launch (the decode path); otherwise it issues the two calls' kernels.
+ *
+ *   logits                                   in   fp32 [T, E], as moe_route
+ *   topk_ids, topk_weights                   out  as moe_route
+ *   expert_offsets, sorted_slots, slot_rows,
+ *   active_experts, num_active               out  as moe_permute
+ *   workspace       scratch, device, >= moe_permute_workspace_bytes(T,
+ *                   top_k, E) bytes (0 when T <= 64; may then be NULL);
+ *                   contents on entry are ignored.
+ *
+ * Errors as moe_route and moe_permute; nothing is enqueued on an error.
+ */
+int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t top_k,
+                      int32_t* topk_ids, float* topk_weights,
+                      int32_t* expert_offsets, int32_t* sorted_slots,
+                      int32_t* slot_rows, int32_t* active_experts,
+                      int32_t* num_active, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Workspace bytes the expert FFN entry points need for these sizes. */
 size_t moe_ffn_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H,
                                int32_t I);

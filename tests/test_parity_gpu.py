@@ -200,6 +200,37 @@ def test_permute_alone_bit_exact(dev, T, E):
     assert int(got["num_active"].item()) == int(ref["num_active"])
 
 
+@pytest.mark.parametrize("T,E,k", [
+    (1, 512, 10), (8, 512, 10), (64, 1024, 64), (64, 64, 1), (5, 37, 5),
+    (65, 512, 10),   # more than 64 tokens: the two-call path
+    (3, 2048, 8),    # more than 1024 experts: the two-call path
+])
+def test_route_permute_matches_separate_calls(dev, T, E, k):
+    """moe_route_permute returns what moe_route then moe_permute return, bit for bit,
+    and the oracle's routing and permutation (ties included: logits repeat)."""
+    from w4a16_group_quantized_amd import ops
+
+    rng = np.random.default_rng(T * 7 + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, E // 3:E // 3 + 4] = logits[:, :4]          # equal logits on other experts
+    lg = torch.from_numpy(logits).to(dev)
+    ids_f, w_f, perm_f = ops.moe_route_permute(lg, k)
+    ids_s, w_s = ops.moe_route(lg, k)
+    perm_s = ops.moe_permute(ids_s, E)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_f, ids_s)
+    assert torch.equal(w_f.view(torch.int32), w_s.view(torch.int32))
+    for key in perm_s:
+        assert torch.equal(perm_f[key], perm_s[key]), key
+    ref_ids, ref_w = oracle.route(logits, k)
+    ref_perm = oracle.permute(ref_ids, E)
+    assert np.array_equal(ids_f.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w_f.cpu().numpy(), ref_w, rtol=0, atol=1e-6)
+    for key in ("expert_offsets", "sorted_slots", "slot_rows", "active_experts"):
+        assert np.array_equal(perm_f[key].cpu().numpy(), ref_perm[key]), key
+    assert int(perm_f["num_active"].item()) == int(ref_perm["num_active"])
+
+
 def test_combine_alone(dev):
     from w4a16_group_quantized_amd import ops
 

@@ -125,6 +125,26 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
   return check_launch();
 }
 
+int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t top_k,
+                      int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                      int32_t* sorted_slots, int32_t* slot_rows, int32_t* active_experts,
+                      int32_t* num_active, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(logits) || !ok_ptr(topk_ids) || !ok_ptr(topk_weights) || !ok_ptr(expert_offsets) ||
+      !ok_ptr(sorted_slots) || !ok_ptr(slot_rows) || !ok_ptr(active_experts) ||
+      !ok_ptr(num_active))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = permute_workspace_bytes(T, E);
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (need > 0 && !ok_ptr(workspace)) return MOE_ERR_INVALID_ARG;
+  launch_route_permute(logits, static_cast<int>(T), E, top_k, topk_ids, topk_weights,
+                       expert_offsets, sorted_slots, slot_rows, active_experts, num_active,
+                       workspace, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
 size_t moe_ffn_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
   if (check_routing(T, top_k, E) != MOE_OK || check_dims(H, I, kGroup) != MOE_OK) return 0;
   return ffn_workspace_bytes(T, top_k, E, H, I);

@@ -28,6 +28,13 @@ void launch_permute(const int* ids, int T, int top_k, int E, int* offsets,
                     int* sorted_slots, int* slot_rows, int* active,
                     int* num_active, void* workspace, hipStream_t stream);
 
+// Router and permutation in one call: one launch when route_permute_fused(T,
+// E) (small T), else the two launches above.
+bool route_permute_fused(int64_t T, int E);
+void launch_route_permute(const float* logits, int T, int E, int top_k, int* ids,
+                          float* weights, int* offsets, int* sorted_slots, int* slot_rows,
+                          int* active, int* num_active, void* workspace, hipStream_t stream);
+
 struct FfnWorkspace {
   uint16_t* act_hi;  // [S, I] fp16, high part of SiLU(gate)*up
   uint16_t* act_lo;  // [S, I] fp16, act - act_hi rounded to fp16

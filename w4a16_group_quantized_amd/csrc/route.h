@@ -1,0 +1,111 @@
+// Router building blocks shared by the router kernel and the fused small-T
+// router + permutation kernel (internal; not part of the public ABI).
+//
+// A logit becomes a 64-bit key: its order-preserving bit pattern (with -0
+// folded onto +0) above the inverted expert index, so the largest key is the
+// largest logit and, among equal logits, the lowest expert index.
+#pragma once
+
+#include <math.h>
+
+#include "common.h"
+
+namespace moe {
+
+__device__ __forceinline__ uint64_t logit_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;   // -0 ranks with +0
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(ord) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+}
+
+__device__ __forceinline__ float key_logit(uint64_t k) {
+  const uint32_t ord = static_cast<uint32_t>(k >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+__device__ __forceinline__ int key_expert(uint64_t k) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(k));
+}
+
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(x >> 32), CTRL, 0xF, 0xF, false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+// Maximum over the wave, returned in every lane.  The row swaps hand each lane
+// its partner 16 (32) lanes away in one of their two results, and the other
+// result is the lane's own value, so the maximum of all three is the pair's.
+__device__ __forceinline__ uint64_t wave_max(uint64_t k) {
+  k = max64(k, dpp64<0xB1>(k));    // quad_perm [1,0,3,2]
+  k = max64(k, dpp64<0x4E>(k));    // quad_perm [2,3,0,1]
+  k = max64(k, dpp64<0x141>(k));   // row_half_mirror
+  k = max64(k, dpp64<0x140>(k));   // row_mirror
+  {
+    const uint32_t lo = static_cast<uint32_t>(k), hi = static_cast<uint32_t>(k >> 32);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    k = max64(k, max64((static_cast<uint64_t>(h[0]) << 32) | l[0], (static_cast<uint64_t>(h[1]) << 32) | l[1]));
+  }
+  {
+    const uint32_t lo = static_cast<uint32_t>(k), hi = static_cast<uint32_t>(k >> 32);
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    k = max64(k, max64((static_cast<uint64_t>(h[0]) << 32) | l[0], (static_cast<uint64_t>(h[1]) << 32) | l[1]));
+  }
+  return k;
+}
+
+// Top-k of one token's E logits (`row`) by one wave: lane l holds the keys of
+// experts l, l + 64, ...; each of the top_k rounds takes the wave maximum of
+// the lanes' best keys and clears the winner.  Lane j < top_k ends with the
+// expert and logit of rank j; every lane gets the logit of rank 0.
+template <int NPL>  // logits per lane; E <= 64 * NPL
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int top_k,
+                                          int& my_id, float& my_logit, float& top_logit) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[NPL];  // 0: absent or taken (every real key is larger)
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? logit_key(row[e], e) : 0ull;
+  }
+  my_id = -1;
+  my_logit = 0.f;
+  top_logit = 0.f;
+  for (int j = 0; j < top_k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < NPL; ++i) best = max64(best, key[i]);
+    best = wave_max(best);
+    const int e = key_expert(best);
+    const bool owner = (e & 63) == lane;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (owner && i == (e >> 6)) key[i] = 0ull;
+    const float v = key_logit(best);
+    if (j == 0) top_logit = v;
+    if (lane == j) {
+      my_id = e;
+      my_logit = v;
+    }
+  }
+}
+
+// Renormalised weight of the lane's rank: exp(l_j - l_0) / sum_j' exp(l_j' -
+// l_0) over the top_k ranks (the full-softmax denominator cancels).  Called
+// by all 64 lanes; meaningful in lanes j < top_k.
+__device__ __forceinline__ float wave_topk_weight(float my_logit, float top_logit, int top_k) {
+  const int lane = threadIdx.x & 63;
+  const float num = (lane < top_k) ? expf(my_logit - top_logit) : 0.f;
+  float den = num;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
+  return num / den;
+}
+
+}  // namespace moe

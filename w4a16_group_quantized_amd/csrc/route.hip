@@ -13,60 +13,12 @@
 // Qwen3.8 Flash Next NVFP4", section "Implemented route".
 #include <math.h>
 
-#include "common.h"
+#include "route.h"
 
 namespace moe {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-
-__device__ __forceinline__ uint64_t logit_key(float v, int e) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;   // -0 ranks with +0
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(ord) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
-}
-
-__device__ __forceinline__ float key_logit(uint64_t k) {
-  const uint32_t ord = static_cast<uint32_t>(k >> 32);
-  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-}
-
-__device__ __forceinline__ int key_expert(uint64_t k) {
-  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(k));
-}
-
-__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t x) {
-  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(x >> 32), CTRL, 0xF, 0xF, false);
-  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
-}
-
-// Maximum over the wave, returned in every lane.  The row swaps hand each lane
-// its partner 16 (32) lanes away in one of their two results, and the other
-// result is the lane's own value, so the maximum of all three is the pair's.
-__device__ __forceinline__ uint64_t wave_max(uint64_t k) {
-  k = max64(k, dpp64<0xB1>(k));    // quad_perm [1,0,3,2]
-  k = max64(k, dpp64<0x4E>(k));    // quad_perm [2,3,0,1]
-  k = max64(k, dpp64<0x141>(k));   // row_half_mirror
-  k = max64(k, dpp64<0x140>(k));   // row_mirror
-  {
-    const uint32_t lo = static_cast<uint32_t>(k), hi = static_cast<uint32_t>(k >> 32);
-    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    k = max64(k, max64((static_cast<uint64_t>(h[0]) << 32) | l[0], (static_cast<uint64_t>(h[1]) << 32) | l[1]));
-  }
-  {
-    const uint32_t lo = static_cast<uint32_t>(k), hi = static_cast<uint32_t>(k >> 32);
-    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    k = max64(k, max64((static_cast<uint64_t>(h[0]) << 32) | l[0], (static_cast<uint64_t>(h[1]) << 32) | l[1]));
-  }
-  return k;
-}
 
 template <int NPL>  // logits per lane; E <= 64 * NPL
 __global__ __launch_bounds__(64 * kWavesPerBlock) void route_topk_kernel(
@@ -75,40 +27,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_topk_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
-  const float* row = logits + static_cast<size_t>(t) * E;
-
-  uint64_t key[NPL];  // 0: absent or taken (every real key is larger)
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? logit_key(row[e], e) : 0ull;
+  int id;
+  float logit, top;
+  wave_topk<NPL>(logits + static_cast<size_t>(t) * E, E, top_k, id, logit, top);
+  const float w = wave_topk_weight(logit, top, top_k);
+  if (lane < top_k) {
+    ids[static_cast<size_t>(t) * top_k + lane] = id;
+    weights[static_cast<size_t>(t) * top_k + lane] = w;
   }
-
-  float mine = 0.f;  // lane j keeps the logit chosen in round j
-  float top = 0.f;   // logit of rank 0
-  for (int j = 0; j < top_k; ++j) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < NPL; ++i) best = max64(best, key[i]);
-    best = wave_max(best);
-    const int e = key_expert(best);
-    const bool owner = (e & 63) == lane;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (owner && i == (e >> 6)) key[i] = 0ull;
-    const float v = key_logit(best);
-    if (j == 0) top = v;
-    if (lane == j) {
-      mine = v;
-      ids[static_cast<size_t>(t) * top_k + j] = e;
-    }
-  }
-
-  const float num = (lane < top_k) ? expf(mine - top) : 0.f;
-  float den = num;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off, 64);
-  if (lane < top_k) weights[static_cast<size_t>(t) * top_k + lane] = num / den;
 }
 
 template <int NPL>

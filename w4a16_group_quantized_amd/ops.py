@@ -31,6 +31,7 @@ EXPORTED = (
     "moe_route",
     "moe_permute_workspace_bytes",
     "moe_permute",
+    "moe_route_permute",
     "moe_ffn_workspace_bytes",
     "moe_w4a16_grouped_ffn",
     "moe_w4a16_gate_up",
@@ -58,6 +59,8 @@ _SIGNATURES = {
     "moe_route": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "moe_permute": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_permute": (
+        ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_ffn_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
     "moe_w4a16_grouped_ffn": (
         ctypes.c_int,
@@ -169,6 +172,33 @@ def moe_permute(topk_ids: torch.Tensor, E: int, workspace: torch.Tensor | None =
     return out
 
 
+def moe_route_permute(logits: torch.Tensor, top_k: int, workspace: torch.Tensor | None = None,
+                      out_ids=None, out_weights=None, out: dict | None = None):
+    """moe_route then moe_permute in one call (one launch for small T): (ids, weights, perm dict)."""
+    lib = load_library()
+    T, E = logits.shape
+    dev = logits.device
+    S = T * top_k
+    ids = out_ids if out_ids is not None else torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = out_weights if out_weights is not None else torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    if out is None:
+        out = {
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "sorted_slots": torch.empty(S, dtype=torch.int32, device=dev),
+            "slot_rows": torch.empty(S, dtype=torch.int32, device=dev),
+            "active_experts": torch.empty(E, dtype=torch.int32, device=dev),
+            "num_active": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+    need = permute_workspace_bytes(T, top_k, E)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    _check("moe_route_permute", lib.moe_route_permute(
+        _ptr(logits), T, E, top_k, _ptr(ids), _ptr(w), _ptr(out["expert_offsets"]),
+        _ptr(out["sorted_slots"]), _ptr(out["slot_rows"]), _ptr(out["active_experts"]),
+        _ptr(out["num_active"]), _ptr(workspace), workspace.numel(), _stream()))
+    return ids, w, out
+
+
 def _ffn_ws(T, k, E, H, I, workspace, dev):
     need = ffn_workspace_bytes(T, k, E, H, I)
     if workspace is None:
@@ -259,8 +289,7 @@ class MoELayer:
         self.out = torch.empty((T, H), dtype=torch.float16, device=dev)
 
     def __call__(self, logits: torch.Tensor, x: torch.Tensor, w: dict) -> torch.Tensor:
-        moe_route(logits, self.top_k, self.ids, self.weights)
-        moe_permute(self.ids, self.E, self.perm_ws, self.perm)
+        moe_route_permute(logits, self.top_k, self.perm_ws, self.ids, self.weights, self.perm)
         moe_w4a16_grouped_ffn(x, self.top_k, self.perm, w, self.y_sorted, self.ffn_ws)
         moe_combine(self.y_sorted, self.weights, self.perm["slot_rows"], self.out)
         return self.out
