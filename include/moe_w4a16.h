@@ -232,6 +232,41 @@ int moe_combine(const float* y_sorted, const float* topk_weights,
                 const int32_t* slot_rows, int64_t T, int32_t top_k, int32_t H,
                 uint16_t* out, void* stream);
 
+/* Workspace bytes moe_layer_forward needs for these sizes. */
+size_t moe_layer_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H,
+                                 int32_t I);
+
+/*
+ * moe_layer_forward - the whole routed-expert layer in one call:
+ * moe_route_permute, moe_w4a16_grouped_ffn and moe_combine on the same
+ * arguments, with the routing, the FFN scratch and y_sorted kept in the
+ * workspace; out is what the four calls produce, bit for bit (the sections
+ * cited above for each step).  For T <= 8 and E <= 1024 (decode) the gate/up
+ * kernel routes the tokens itself, every workgroup the same way, which saves
+ * the router/permutation launch.
+ *
+ *   logits      in   fp32 [T, E]
+ *   x           in   fp16 [T, H]
+ *   w13_*, w2_* in   as moe_w4a16_grouped_ffn
+ *   group_size  must be 32
+ *   out         out  fp16 [T, H]
+ *   workspace   scratch, device, >= moe_layer_workspace_bytes(...) bytes;
+ *               contents on entry are ignored.  After the call it holds, in
+ *               order and each 256-byte aligned: topk_ids [S], topk_weights
+ *               [S], expert_offsets [E+1], sorted_slots [S], slot_rows [S],
+ *               active_experts [E], num_active [1], the permutation
+ *               workspace, the FFN workspace and y_sorted [S, H].
+ *
+ * Errors as the calls it stands for; nothing is enqueued on an error.
+ */
+int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T,
+                      int32_t E, int32_t top_k, const int32_t* w13_qweight,
+                      const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                      const int32_t* w2_qweight, const uint16_t* w2_scales,
+                      const int32_t* w2_qzeros, int32_t H, int32_t I,
+                      int32_t group_size, uint16_t* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -126,3 +126,36 @@ def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ops, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ops.load_library(str(tmp_path / "nope.so"))
+
+
+def test_route_permute_rejects_bad_arguments():
+    lib = ops.load_library()
+    out = [FAKE] * 7
+    assert lib.moe_route_permute(None, 4, 8, 2, *out, None, 0, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_permute(FAKE, 4, 8, 9, *out, None, 0, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_permute(FAKE, 4, 5000, 2, *out, None, 0, None) == ops.MOE_ERR_UNSUPPORTED
+    # more than 64 tokens need the permutation workspace
+    assert lib.moe_route_permute(FAKE, 100, 512, 10, *out, FAKE, 0, None) == ops.MOE_ERR_WORKSPACE
+    assert lib.moe_route_permute(None, 0, 8, 2, *([None] * 7), None, 0, None) == ops.MOE_OK
+
+
+def _layer(lib, T=8, E=512, k=10, H=2560, I=640, gs=32, ws_bytes=None, logits=FAKE, out=FAKE):
+    need = ops.layer_workspace_bytes(T, k, E, H, I) if ws_bytes is None else ws_bytes
+    w = [FAKE] * 6
+    return lib.moe_layer_forward(logits, FAKE, T, E, k, *w, H, I, gs, out, FAKE, need, None)
+
+
+def test_layer_workspace_and_arguments():
+    lib = ops.load_library()
+    need = ops.layer_workspace_bytes(8, 10, 512, 2560, 640)
+    # routing, the FFN workspace and y_sorted [S, H] fp32 all live in it
+    assert need >= ops.ffn_workspace_bytes(8, 10, 512, 2560, 640) + 80 * 2560 * 4
+    assert ops.layer_workspace_bytes(8, 10, 512, 2561, 640) == 0
+    assert _layer(lib, gs=64) == ops.MOE_ERR_UNSUPPORTED
+    assert _layer(lib, H=2561) == ops.MOE_ERR_INVALID_ARG
+    assert _layer(lib, k=0) == ops.MOE_ERR_INVALID_ARG
+    assert _layer(lib, logits=None) == ops.MOE_ERR_INVALID_ARG
+    assert _layer(lib, out=FAKE + 2) == ops.MOE_ERR_INVALID_ARG
+    assert _layer(lib, ws_bytes=need - 1) == ops.MOE_ERR_WORKSPACE
+    assert _layer(lib, T=0) == ops.MOE_OK
+    assert _layer(lib, T=(1 << 31) // 2560 + 1, k=1) == ops.MOE_ERR_UNSUPPORTED

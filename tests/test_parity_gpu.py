@@ -231,6 +231,49 @@ def test_route_permute_matches_separate_calls(dev, T, E, k):
     assert int(perm_f["num_active"].item()) == int(ref_perm["num_active"])
 
 
+@pytest.mark.parametrize("E,k,H,I,T", [
+    (512, 10, 2560, 640, 8),    # the decode workload: routing inside the gate/up kernel
+    (512, 10, 2560, 160, 1),
+    (64, 6, 512, 256, 2),
+    (2048, 8, 256, 128, 4),     # more than 1024 experts: routing as its own launch
+    (64, 6, 512, 256, 9),       # more than 8 tokens: the matrix-core path
+])
+def test_layer_forward_matches_the_four_calls(dev, E, k, H, I, T):
+    """moe_layer_forward gives the four calls' out, routing and y_sorted, bit for bit."""
+    from w4a16_group_quantized_amd import ops
+
+    shape = synth.MoEShape(E=E, top_k=k, H=H, I=I, T=T)
+    host = synth.make_inputs(shape, 3)
+    w = ops.weights_to_device(host, dev)
+    logits = torch.from_numpy(host["logits"]).to(dev)
+    x = torch.from_numpy(host["x"]).to(dev)
+    layer = ops.MoELayer(T, E, k, H, I, dev)
+    ref = layer(logits, x, w).clone()
+    got = layer.forward(logits, x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    v = layer.forward_views()
+    assert torch.equal(v["topk_ids"], layer.ids)
+    assert torch.equal(v["topk_weights"].view(torch.int32), layer.weights.view(torch.int32))
+    for key in ("expert_offsets", "sorted_slots", "slot_rows", "active_experts", "num_active"):
+        assert torch.equal(v[key], layer.perm[key]), key
+    assert torch.equal(v["y_sorted"].view(torch.int32), layer.y_sorted.view(torch.int32))
+
+
+def test_layer_forward_against_oracle(dev):
+    from w4a16_group_quantized_amd import ops
+
+    shape = synth.MoEShape(E=64, top_k=6, H=512, I=256, T=8)
+    host = synth.make_inputs(shape, 11)
+    ids, wts = oracle.route(host["logits"], shape.top_k)
+    w = ops.weights_to_device(host, dev)
+    out = ops.moe_layer_forward(torch.from_numpy(host["logits"]).to(dev),
+                                torch.from_numpy(host["x"]).to(dev), shape.top_k, w)
+    torch.cuda.synchronize()
+    sub = oracle.token_outputs(host, ids, wts, np.arange(shape.T))
+    assert_fp16_close(out.cpu().numpy(), sub, f"{shape} moe_layer_forward")
+
+
 def test_combine_alone(dev):
     from w4a16_group_quantized_amd import ops
 

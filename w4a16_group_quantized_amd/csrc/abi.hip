@@ -262,4 +262,115 @@ int moe_combine(const float* y_sorted, const float* topk_weights, const int32_t*
   return check_launch();
 }
 
+// ---- the whole layer ---------------------------------------------------------
+// Workspace: the routing arrays (ids, weights, offsets, sorted slots, slot
+// rows, active list, active count), the permutation and FFN workspaces and
+// y_sorted, each 256-byte aligned.
+struct LayerWs {
+  int32_t* ids;
+  float* weights;
+  int32_t* offsets;
+  int32_t* sorted;
+  int32_t* slot_rows;
+  int32_t* active;
+  int32_t* num_active;
+  void* perm;
+  size_t perm_bytes;
+  void* ffn;
+  size_t ffn_bytes;
+  float* y;
+  size_t total;
+};
+
+static LayerWs layer_ws(void* base, int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
+  const size_t S = static_cast<size_t>(T) * top_k;
+  char* p = static_cast<char*>(base);
+  size_t at = 0;
+  auto take = [&](size_t n) {
+    char* q = p ? p + at : nullptr;
+    at += align256(n);
+    return q;
+  };
+  LayerWs w;
+  w.ids = reinterpret_cast<int32_t*>(take(4 * S));
+  w.weights = reinterpret_cast<float*>(take(4 * S));
+  w.offsets = reinterpret_cast<int32_t*>(take(4 * (static_cast<size_t>(E) + 1)));
+  w.sorted = reinterpret_cast<int32_t*>(take(4 * S));
+  w.slot_rows = reinterpret_cast<int32_t*>(take(4 * S));
+  w.active = reinterpret_cast<int32_t*>(take(4 * static_cast<size_t>(E)));
+  w.num_active = reinterpret_cast<int32_t*>(take(4));
+  w.perm_bytes = permute_workspace_bytes(T, E);
+  w.perm = take(w.perm_bytes);
+  w.ffn_bytes = ffn_workspace_bytes(T, top_k, E, H, I);
+  w.ffn = take(w.ffn_bytes);
+  w.y = reinterpret_cast<float*>(take(4 * S * static_cast<size_t>(H)));
+  w.total = at;
+  return w;
+}
+
+size_t moe_layer_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
+  if (check_routing(T, top_k, E) != MOE_OK || check_dims(H, I, kGroup) != MOE_OK) return 0;
+  return layer_ws(nullptr, T, top_k, E, H, I).total;
+}
+
+int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t E, int32_t top_k,
+                      const int32_t* w13_qweight, const uint16_t* w13_scales,
+                      const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                      const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t H, int32_t I,
+                      int32_t group_size, uint16_t* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (int st = check_dims(H, I, group_size)) return st;
+  if (int st = check_prefill(T, top_k, E, H, I)) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) ||
+      !ok_ptr(w13_qzeros) || !ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) ||
+      !ok_ptr(out) || !ok_ptr(workspace))
+    return MOE_ERR_INVALID_ARG;
+  const LayerWs w = layer_ws(workspace, T, top_k, E, H, I);
+  if (workspace_bytes < w.total) return MOE_ERR_WORKSPACE;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (route_in_gate_up(T, E)) {
+    // decode: the gate/up kernel routes the tokens itself
+    const FfnWorkspace fws = ffn_workspace_carve(w.ffn, T, top_k, E, H, I);
+    GateUpArgs a{};
+    a.x = x;
+    a.T = static_cast<int>(T);
+    a.top_k = top_k;
+    a.E = E;
+    a.H = H;
+    a.I = I;
+    a.qw = w13_qweight;
+    a.sc = w13_scales;
+    a.qz = w13_qzeros;
+    const RouteOut r{w.ids, w.weights, w.offsets, w.sorted, w.slot_rows, w.active, w.num_active};
+    launch_route_gate_up_decode(logits, a, r, fws, st);
+    DownArgs d{};
+    d.T = static_cast<int>(T);
+    d.top_k = top_k;
+    d.E = E;
+    d.H = H;
+    d.I = I;
+    d.offsets = w.offsets;
+    d.active = w.active;
+    d.num_active = w.num_active;
+    d.qw = w2_qweight;
+    d.sc = w2_scales;
+    d.qz = w2_qzeros;
+    d.y = w.y;
+    launch_down_decode(d, fws, st);
+  } else {
+    launch_route_permute(logits, static_cast<int>(T), E, top_k, w.ids, w.weights, w.offsets,
+                         w.sorted, w.slot_rows, w.active, w.num_active, w.perm, st);
+    if (int e = check_launch()) return e;
+    if (int e = moe_w4a16_grouped_ffn(x, T, top_k, w.offsets, w.sorted, w.active, w.num_active,
+                                      w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
+                                      w2_qzeros, E, H, I, group_size, w.y, w.ffn, w.ffn_bytes,
+                                      stream))
+      return e;
+  }
+  launch_combine(w.y, w.weights, w.slot_rows, static_cast<int>(T), top_k, H, out, st);
+  return check_launch();
+}
+
 }  // extern "C"

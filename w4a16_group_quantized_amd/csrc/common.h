@@ -69,6 +69,23 @@ struct DownArgs {
   float* y;
 };
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
+
+// Stage 1 of the decode FFN that first routes the T tokens itself, from
+// logits [T, E] (route_in_gate_up(T, E): T <= kDecodeMaxT, E <= 1024), and
+// writes the routing out as moe_route_permute does.  The routing fields of
+// `a` (offsets, sorted_slots, active, num_active) are not read.
+struct RouteOut {
+  int* ids;
+  float* weights;
+  int* offsets;
+  int* sorted_slots;
+  int* slot_rows;
+  int* active;
+  int* num_active;
+};
+bool route_in_gate_up(int64_t T, int E);
+void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const RouteOut& r,
+                                 const FfnWorkspace& ws, hipStream_t stream);
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 
 // Matrix-core variant: a prep kernel (tile list built from the routing, x

@@ -45,6 +45,8 @@
 #include <math.h>
 
 #include "common.h"
+#include "permute.h"
+#include "route.h"
 
 namespace moe {
 namespace {
@@ -227,7 +229,26 @@ struct DecodeArgs {
   uint16_t* act_hi;        // stage 1 outputs
   uint16_t* act_lo;
   float* y;                // stage 2 output
+  // stage 1 that routes the tokens itself: logits in; the routing (as
+  // moe_route_permute returns it) written out by workgroup 0
+  const float* logits;
+  int E;
+  int* r_ids;
+  float* r_weights;
+  int* r_offsets;
+  int* r_sorted;
+  int* r_slot_rows;
+  int* r_active;
+  int* r_num_active;
 };
+
+// LDS bytes of the routing tables of a kernel that routes (T <= 64 tokens,
+// E <= 1024 experts): token masks, offsets, active list, sorted slots, slot
+// experts, the active count and the scans' wave totals.
+__host__ __device__ inline size_t route_lds_bytes(int E, int S) {
+  const size_t b = 8ull * E + 4ull * (E + 1) + 4ull * E + 8ull * S + 4 + 4 * (kScanThreads / 64 + 1);
+  return (b + 15) & ~static_cast<size_t>(15);
+}
 
 // Scale halves of one unit: the R rows of its block (stage 1: R/2 gate rows,
 // then R/2 up rows), G each; R * G = 64 * spb.
@@ -307,7 +328,11 @@ struct WinExpert {
   int e, r0, rows;
 };
 
-template <bool GATE_UP, int NA>
+// NPL > 0 (stage 1 only): the workgroup first routes the tokens itself, with
+// the router's and permutation's own steps (route.h, permute.h), from
+// logits of E <= 64 NPL experts; workgroup 0 writes the routing out.  Every
+// workgroup computes the same routing, so none waits for another.
+template <bool GATE_UP, int NA, int NPL>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo) {
   // 16-byte aligned: fragments and scales are read with 16-byte LDS loads,
   // and the static counter below would otherwise shift the dynamic area
@@ -327,7 +352,71 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   uint32_t* frags = lds;
   uint16_t* scales = reinterpret_cast<uint16_t*>(lds + kXE * NF * G * kFragDwords);
 
-  const int n_active = *p.num_active;
+  // ---- routing: from the caller's arrays, or computed here (NPL > 0)
+  int* ract = nullptr;     // LDS: active list, offsets, sorted slots
+  int* roff = nullptr;
+  int* rsorted = nullptr;
+  int n_active;
+  if constexpr (NPL > 0) {
+    const int E = p.E, S = p.T * p.top_k;
+    const int tid = threadIdx.x;
+    auto* rmask = reinterpret_cast<unsigned long long*>(scales + geo.wmax * unit_scale_halves(spb));
+    roff = reinterpret_cast<int*>(rmask + E);
+    ract = roff + E + 1;
+    rsorted = ract + E;
+    int* rslot = rsorted + S;
+    int* rnum = rslot + S;
+    int* wtot = rnum + 1;
+    for (int e = tid; e < E; e += kThreads) rmask[e] = 0ull;
+    __syncthreads();
+    for (int t = wave; t < p.T; t += kWaves) {
+      int id;
+      float logit, top;
+      wave_topk<NPL>(p.logits + static_cast<size_t>(t) * E, E, p.top_k, id, logit, top);
+      const float w = wave_topk_weight(logit, top, p.top_k);
+      if (lane < p.top_k) {
+        const int sl = t * p.top_k + lane;
+        rslot[sl] = id;
+        atomicOr(&rmask[id], 1ull << t);
+        if (blockIdx.x == 0) {
+          p.r_ids[sl] = id;
+          p.r_weights[sl] = w;
+        }
+      }
+    }
+    __syncthreads();
+    int cnt[kPerThread], off[kPerThread];
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int e = kPerThread * tid + i;
+      cnt[i] = (e < E) ? __popcll(rmask[e]) : 0;
+    }
+    write_offsets_and_active(cnt, E, S, roff, ract, rnum, wtot, off);
+    __syncthreads();
+    for (int sl = tid; sl < S; sl += kThreads) {
+      const int t = sl / p.top_k;
+      const int e = rslot[sl];
+      const int r = roff[e] + __popcll(rmask[e] & ((1ull << t) - 1ull));
+      rsorted[r] = sl;
+      if (blockIdx.x == 0) {
+        p.r_sorted[r] = sl;
+        p.r_slot_rows[sl] = r;
+      }
+    }
+    if (blockIdx.x == 0) {
+      for (int e = tid; e <= E; e += kThreads) p.r_offsets[e] = roff[e];
+      for (int e = tid; e < E; e += kThreads) p.r_active[e] = ract[e];
+      if (tid == 0) *p.r_num_active = *rnum;
+    }
+    __syncthreads();
+    n_active = *rnum;
+  } else {
+    n_active = *p.num_active;
+  }
+  auto active_at = [&](int a) { if constexpr (NPL > 0) return ract[a]; else return p.active[a]; };
+  auto offset_at = [&](int e) { if constexpr (NPL > 0) return roff[e]; else return p.offsets[e]; };
+  auto sorted_at = [&](int r) { if constexpr (NPL > 0) return rsorted[r]; else return p.sorted_slots[r]; };
+
   const int64_t U = static_cast<int64_t>(n_active) * nb;
   const int u0 = static_cast<int>(U * blockIdx.x / geo.nwg);
   const int u1 = static_cast<int>(U * (blockIdx.x + 1) / geo.nwg);
@@ -341,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
     // has a row)
     int xe[kXE], xr0[kXE] = {0, 0}, xrows[kXE] = {1, 1};
 #pragma unroll
-    for (int i = 0; i < kXE; ++i) xe[i] = i < nx ? p.active[a0 + i] : 0;
+    for (int i = 0; i < kXE; ++i) xe[i] = i < nx ? active_at(a0 + i) : 0;
     int maxrows = 1;
     for (int c = 0; c < maxrows; c += NA) {
       if (w0 != u0 || c != 0) lds_barrier();  // the previous pass no longer reads LDS
@@ -403,8 +492,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
       if (c == 0) {
 #pragma unroll
         for (int i = 0; i < kXE; ++i) {
-          xr0[i] = i < nx ? p.offsets[xe[i]] : 0;
-          xrows[i] = i < nx ? p.offsets[xe[i] + 1] - xr0[i] : 0;
+          xr0[i] = i < nx ? offset_at(xe[i]) : 0;
+          xrows[i] = i < nx ? offset_at(xe[i] + 1) - xr0[i] : 0;
           maxrows = max(maxrows, xrows[i]);
         }
       }
@@ -419,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
           const int r = pick(xr0, xi) + m;
           const uint16_t* src;
           if (GATE_UP) {
-            src = p.x + static_cast<size_t>(p.sorted_slots[r] / p.top_k) * H;
+            src = p.x + static_cast<size_t>(sorted_at(r) / p.top_k) * H;
           } else {
             src = ((f & 1) ? p.a_lo : p.a_hi) + static_cast<size_t>(r) * I;
           }
@@ -575,8 +664,8 @@ size_t frag_bytes(const Geom& geo, int na) {
 // size, from the LDS a workgroup may hold.  Windows aim to cover a
 // workgroup's whole share of units, which is at most ceil(slots * nb / nwg).
 template <bool GATE_UP>
-int plan(Geom& geo, int T, int slots, const DeviceInfo& dev) {
-  const size_t budget = static_cast<size_t>(dev.lds) - 256;
+int plan(Geom& geo, int T, int slots, const DeviceInfo& dev, size_t reserved) {
+  const size_t budget = static_cast<size_t>(dev.lds) - 256 - reserved;
   const size_t unit = static_cast<size_t>(unit_scale_halves(geo.spb)) * 2;
   const int want = static_cast<int>((static_cast<int64_t>(slots) * geo.nb + geo.nwg - 1) / geo.nwg) + 1;
   int na = T >= 2 ? 2 : 1;
@@ -595,17 +684,33 @@ size_t launch_lds(const Geom& geo, int na) {
          static_cast<size_t>(geo.wmax) * unit_scale_halves(geo.spb) * 2;
 }
 
-template <bool GATE_UP>
-void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream) {
-  const DeviceInfo dev = device_info();
-  geo.nwg = dev.cus;
-  const int na = plan<GATE_UP>(geo, p.T, slots, dev);
-  const size_t lds = launch_lds<GATE_UP>(geo, na);
+template <bool GATE_UP, int NPL>
+void launch_decode_npl(const DecodeArgs& p, Geom geo, int na, size_t lds, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(geo.nwg)), block(kThreads);
   if (na == 2)
-    hipLaunchKernelGGL((decode_kernel<GATE_UP, 2>), grid, block, lds, stream, p, geo);
+    hipLaunchKernelGGL((decode_kernel<GATE_UP, 2, NPL>), grid, block, lds, stream, p, geo);
   else
-    hipLaunchKernelGGL((decode_kernel<GATE_UP, 1>), grid, block, lds, stream, p, geo);
+    hipLaunchKernelGGL((decode_kernel<GATE_UP, 1, NPL>), grid, block, lds, stream, p, geo);
+}
+
+// route: stage 1 routes the tokens itself (p.logits, p.E <= 1024, T <= 64).
+template <bool GATE_UP>
+void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream, bool route) {
+  const DeviceInfo dev = device_info();
+  geo.nwg = dev.cus;
+  const size_t rbytes = route ? route_lds_bytes(p.E, p.T * p.top_k) : 0;
+  const int na = plan<GATE_UP>(geo, p.T, slots, dev, rbytes);
+  const size_t lds = launch_lds<GATE_UP>(geo, na) + rbytes;
+  if constexpr (GATE_UP) {
+    if (route) {
+      if (p.E <= 64) return launch_decode_npl<true, 1>(p, geo, na, lds, stream);
+      if (p.E <= 128) return launch_decode_npl<true, 2>(p, geo, na, lds, stream);
+      if (p.E <= 256) return launch_decode_npl<true, 4>(p, geo, na, lds, stream);
+      if (p.E <= 512) return launch_decode_npl<true, 8>(p, geo, na, lds, stream);
+      return launch_decode_npl<true, 16>(p, geo, na, lds, stream);
+    }
+  }
+  launch_decode_npl<GATE_UP, 0>(p, geo, na, lds, stream);
 }
 
 }  // namespace
@@ -632,7 +737,40 @@ void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStrea
   p.I = a.I;
   p.act_hi = ws.act_hi;
   p.act_lo = ws.act_lo;
-  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream);
+  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, false);
+}
+
+bool route_in_gate_up(int64_t T, int E) { return T <= kDecodeMaxT && E <= 1024; }
+
+void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const RouteOut& r,
+                                 const FfnWorkspace& ws, hipStream_t stream) {
+  Geom geo{};
+  geo.G = a.H / kGroup;
+  geo.C = cluster_lanes(geo.G);
+  geo.spb = geo.G / geo.C;
+  const int half = (64 / geo.C) / 2;
+  geo.nb = (a.I + half - 1) / half;
+  DecodeArgs p{};
+  p.x = a.x;
+  p.qw = a.qw;
+  p.sc = a.sc;
+  p.qz = a.qz;
+  p.T = a.T;
+  p.top_k = a.top_k;
+  p.H = a.H;
+  p.I = a.I;
+  p.act_hi = ws.act_hi;
+  p.act_lo = ws.act_lo;
+  p.logits = logits;
+  p.E = a.E;
+  p.r_ids = r.ids;
+  p.r_weights = r.weights;
+  p.r_offsets = r.offsets;
+  p.r_sorted = r.sorted_slots;
+  p.r_slot_rows = r.slot_rows;
+  p.r_active = r.active;
+  p.r_num_active = r.num_active;
+  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, true);
 }
 
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
@@ -655,7 +793,7 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
   p.H = a.H;
   p.I = a.I;
   p.y = a.y;
-  launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream);
+  launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream, false);
 }
 
 }  // namespace moe

@@ -37,6 +37,8 @@ EXPORTED = (
     "moe_w4a16_gate_up",
     "moe_w4a16_down",
     "moe_combine",
+    "moe_layer_workspace_bytes",
+    "moe_layer_forward",
 )
 
 
@@ -76,6 +78,10 @@ _SIGNATURES = {
         [_I64, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P],
     ),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_layer_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
+    "moe_layer_forward": (
+        ctypes.c_int,
+        [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
 }
 
 
@@ -264,6 +270,52 @@ def moe_combine(y_sorted: torch.Tensor, topk_weights: torch.Tensor, slot_rows: t
     return out
 
 
+def layer_workspace_bytes(T: int, top_k: int, E: int, H: int, I: int) -> int:
+    return int(load_library().moe_layer_workspace_bytes(T, top_k, E, H, I))
+
+
+def layer_workspace_views(ws: torch.Tensor, T: int, top_k: int, E: int, H: int, I: int) -> dict:
+    """The routing and y_sorted inside a moe_layer_forward workspace (layout of the header)."""
+    S = T * top_k
+
+    def a256(n):
+        return (n + 255) & ~255
+
+    sizes = [("topk_ids", 4 * S), ("topk_weights", 4 * S), ("expert_offsets", 4 * (E + 1)),
+             ("sorted_slots", 4 * S), ("slot_rows", 4 * S), ("active_experts", 4 * E),
+             ("num_active", 4), ("perm_ws", permute_workspace_bytes(T, top_k, E)),
+             ("ffn_ws", ffn_workspace_bytes(T, top_k, E, H, I)), ("y_sorted", 4 * S * H)]
+    views, at = {}, 0
+    for name, n in sizes:
+        views[name] = ws[at:at + n]
+        at += a256(n)
+    out = {k: views[k].view(torch.int32) for k in ("topk_ids", "sorted_slots", "slot_rows",
+                                                   "expert_offsets", "active_experts", "num_active")}
+    out["topk_ids"] = out["topk_ids"].view(T, top_k)
+    out["topk_weights"] = views["topk_weights"].view(torch.float32).view(T, top_k)
+    out["y_sorted"] = views["y_sorted"].view(torch.float32).view(S, H)
+    return out
+
+
+def moe_layer_forward(logits: torch.Tensor, x: torch.Tensor, top_k: int, w: dict,
+                      workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """The whole layer in one call: logits fp32 [T, E], x fp16 [T, H] -> out fp16 [T, H]."""
+    lib = load_library()
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w["w2_q"].shape[2] * 8
+    dev = x.device
+    if workspace is None:
+        workspace = _workspace(layer_workspace_bytes(T, top_k, E, H, I), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float16, device=dev)
+    _check("moe_layer_forward", lib.moe_layer_forward(
+        _ptr(logits), _ptr(x), T, E, top_k, _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w13_z"]),
+        _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]), H, I, GROUP_SIZE, _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
 # --------------------------------------------------------------------------- #
 # one whole layer call
 # --------------------------------------------------------------------------- #
@@ -287,12 +339,21 @@ class MoELayer:
         self.ffn_ws = _workspace(ffn_workspace_bytes(T, top_k, E, H, I), dev)
         self.y_sorted = torch.empty((S, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H), dtype=torch.float16, device=dev)
+        self.layer_ws = _workspace(layer_workspace_bytes(T, top_k, E, H, I), dev)
+        self.fused_out = torch.empty((T, H), dtype=torch.float16, device=dev)
 
     def __call__(self, logits: torch.Tensor, x: torch.Tensor, w: dict) -> torch.Tensor:
         moe_route_permute(logits, self.top_k, self.perm_ws, self.ids, self.weights, self.perm)
         moe_w4a16_grouped_ffn(x, self.top_k, self.perm, w, self.y_sorted, self.ffn_ws)
         moe_combine(self.y_sorted, self.weights, self.perm["slot_rows"], self.out)
         return self.out
+
+    def forward(self, logits: torch.Tensor, x: torch.Tensor, w: dict) -> torch.Tensor:
+        """The same layer through moe_layer_forward (one call; routing kept in layer_ws)."""
+        return moe_layer_forward(logits, x, self.top_k, w, self.layer_ws, self.fused_out)
+
+    def forward_views(self) -> dict:
+        return layer_workspace_views(self.layer_ws, self.T, self.top_k, self.E, self.H, self.I)
 
 
 def weights_to_device(host: dict, device="cuda") -> dict:
