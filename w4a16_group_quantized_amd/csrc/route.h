@@ -60,11 +60,28 @@ __device__ __forceinline__ uint64_t wave_max(uint64_t k) {
   return k;
 }
 
+// Maximum of a 32-bit value over the wave, in every lane: DPP within rows of
+// 16 lanes, then the row swaps (each hands a lane its partner 16 or 32 lanes
+// away in one of its two results, the lane's own value in the other).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(v, max(a[0], a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(v, max(b[0], b[1]));
+}
+
 // Top-k of one token's E logits (`row`) by one wave: lane l holds the keys of
-// experts l, l + 64, ...; each of the top_k rounds takes the wave maximum of
-// the lanes' best keys and clears the winner.  Lane j < top_k ends with the
-// expert and logit of rank j; every lane gets the logit of rank 0.
-template <int NPL>  // logits per lane; E <= 64 * NPL
+// experts l, l + 64, ..., sorted once in descending order; each of the top_k
+// rounds takes the wave maximum of the lanes' first keys and the winning lane
+// drops its first key.  The wave maximum of a 64-bit key is taken in two
+// 32-bit passes (upper word, then the lower word among the lanes that hold
+// the maximal upper word), which is the same maximum.  Lane j < top_k ends
+// with the expert and logit of rank j; every lane gets the logit of rank 0.
+template <int NPL>  // logits per lane; E <= 64 * NPL, NPL a power of two
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int top_k,
                                           int& my_id, float& my_logit, float& top_logit) {
   const int lane = threadIdx.x & 63;
@@ -74,19 +91,37 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
     const int e = lane + 64 * i;
     key[i] = e < E ? logit_key(row[e], e) : 0ull;
   }
+  // bitonic sort, descending
+#pragma unroll
+  for (int size = 2; size <= NPL; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool desc = (i & size) == 0;
+          const uint64_t a = key[i], b = key[j];
+          const bool swap = desc ? a < b : a > b;
+          key[i] = swap ? b : a;
+          key[j] = swap ? a : b;
+        }
+      }
   my_id = -1;
   my_logit = 0.f;
   top_logit = 0.f;
   for (int j = 0; j < top_k; ++j) {
-    uint64_t best = key[0];
+    const uint32_t hi = static_cast<uint32_t>(key[0] >> 32), lo = static_cast<uint32_t>(key[0]);
+    const uint32_t mhi = wave_max_u32(hi);
+    const uint32_t mlo = wave_max_u32(hi == mhi ? lo : 0u);
+    const uint64_t best = (static_cast<uint64_t>(mhi) << 32) | mlo;
+    // the winning lane drops its first key (written with masks: as selects the
+    // compiler turns the shift into an indexed pick over all slots)
+    const uint64_t m = key[0] == best ? ~0ull : 0ull;
 #pragma unroll
-    for (int i = 1; i < NPL; ++i) best = max64(best, key[i]);
-    best = wave_max(best);
+    for (int i = 0; i + 1 < NPL; ++i) key[i] = (key[i + 1] & m) | (key[i] & ~m);
+    key[NPL - 1] &= ~m;
     const int e = key_expert(best);
-    const bool owner = (e & 63) == lane;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      if (owner && i == (e >> 6)) key[i] = 0ull;
     const float v = key_logit(best);
     if (j == 0) top_logit = v;
     if (lane == j) {
