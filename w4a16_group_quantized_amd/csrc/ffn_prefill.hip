@@ -55,9 +55,12 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = kWaves * kSub;         // weight rows per N-tile
 constexpr int kBlockHalfs = 64 * 8;        // one fragment block: 64 lanes x 8 fp16
 constexpr int kBufferFlags = 0x00020000;   // buffer descriptor word 3 for raw dword access on gfx9
-// Cost of a work item in 32-row subtiles: its live subtiles plus this base
+// Cost of a work item: kSubCost per live 32-row subtile plus kItemBase
 // (weight streaming and per-group vector work do not shrink with the rows).
-constexpr int kItemBase = 4;
+// Measured item durations grow about 11 us per subtile above a 17 us floor
+// at the 4096-token shape, a base about 1.5 times the per-subtile cost.
+constexpr int kSubCost = 2;
+constexpr int kItemBase = 3;
 
 // Groups per LDS stage: deeper for 32-row tiles, which stream weights with
 // little arithmetic per byte, so more bytes must be in flight per wave.
@@ -539,7 +542,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tot) {
 // k-slot order within every 8-wide block.
 __global__ __launch_bounds__(1024) void prefill_prep_kernel(
     const int* __restrict__ offsets, const int* __restrict__ active,
-    const int* __restrict__ num_active, int bm, int base, int nn_gate_up, int nn_down,
+    const int* __restrict__ num_active, int bm, int sub_cost, int base, int nn_gate_up, int nn_down,
     int* __restrict__ tiles, int* __restrict__ tile_count, int* __restrict__ sched,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int64_t chunks) {
   if (blockIdx.x > 0) {
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(
       const int e = active[a];
       const int rows = offsets[e + 1] - offsets[e];
       cnt[i] = (rows + bm - 1) / bm;
-      wk[i] = (rows + kSub - 1) / kSub + base * cnt[i];
+      wk[i] = sub_cost * ((rows + kSub - 1) / kSub) + base * cnt[i];
     }
     csum += cnt[i];
     wsum += wk[i];
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(
     const int64_t r = target - static_cast<int64_t>(work0[lo]) * nn;
     const int ntl = tile0[lo + 1] - tile0[lo];
     const int wa = work0[lo + 1] - work0[lo];
-    const int wfull = msub + base;   // work of a full tile
+    const int wfull = sub_cost * msub + base;   // work of a full tile
     const int u = static_cast<int>(min<int64_t>(r / (static_cast<int64_t>(wfull) * nn), ntl - 1));
     const int w = min(wfull, wa - u * wfull);
     const int64_t r2 = r - static_cast<int64_t>(u) * wfull * nn;
@@ -632,9 +635,10 @@ int64_t max_tiles(int64_t S, int E) {
   return (S + bm - 1) / bm + std::min<int64_t>(E, S);
 }
 
-// Workgroups per range.  An item of s live subtiles costs s + kItemBase, at
-// least 1 + kItemBase and at most (1 + kItemBase) s, so a range (1/8 of the
-// cost) holds at most 1/8 of the items' subtiles plus one item.  The subtiles
+// Workgroups per range.  An item of s live subtiles costs
+// c = kSubCost s + kItemBase, at least c1 = kSubCost + kItemBase and at most
+// c1 s, so a range (1/8 of the cost) holds at most 1/8 of the items'
+// subtiles plus one item.  The subtiles
 // number at most one per 32 rows plus one per expert.
 int64_t range_bound(int64_t S, int E, int n_ntiles) {
   const int64_t subtiles = (S + kSub - 1) / kSub + std::min<int64_t>(E, S);
@@ -671,8 +675,8 @@ void launch_prefill_prep(const uint16_t* x, int T, int H, int I, const int* offs
   const int64_t chunks = static_cast<int64_t>(T) * H / 8;
   const unsigned blocks = 1 + static_cast<unsigned>((chunks + 1023) / 1024);
   hipLaunchKernelGGL(prefill_prep_kernel, dim3(blocks), dim3(1024), 0, stream, offsets, active,
-                     num_active, tile_rows(S, E), kItemBase, ntiles_gate_up(I), ntiles_down(H), ws.tiles,
-                     ws.tile_count, ws.sched, x, ws.x_perm, chunks);
+                     num_active, tile_rows(S, E), kSubCost, kItemBase, ntiles_gate_up(I),
+                     ntiles_down(H), ws.tiles, ws.tile_count, ws.sched, x, ws.x_perm, chunks);
 }
 
 void launch_gate_up_prefill(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
