@@ -29,6 +29,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -53,6 +54,9 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=480)
     p.add_argument("--warmup", type=int, default=48)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--tokens", type=int, default=None,
+                   help="token count T instead of the workload's (the inputs of a smaller T are the "
+                        "first rows of the workload's at the same seed), e.g. the 1/2/4/8 decode sweep")
     p.add_argument("--layers", type=int, default=16, help="device copies of the expert weights")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-graph", action="store_true", help="report the eager loop as value")
@@ -215,6 +219,11 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     shape = synth.WORKLOADS[args.workload]
+    if args.tokens is not None and args.tokens != shape.T:
+        shape = dataclasses.replace(shape, T=args.tokens)
+        shape.validate()
+    # byte counters were taken at the workload's own token count only
+    counters_apply = shape.T == synth.WORKLOADS[args.workload].T
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ops.load_library()
@@ -358,7 +367,7 @@ def main(argv=None) -> int:
         roof = {"bound": "mfma", "achieved": work["gate_up_flops"] / gate_up_s / 1e12,
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = counter_traffic(args.workload, "gate_up")
+    roof["traffic"] = counter_traffic(args.workload, "gate_up") if counters_apply else None
     roof.update({
         "kernel": "gate/up kernel of moe_w4a16_gate_up",
         "avg_launch_us": gate_up_ms * 1e3,
@@ -399,7 +408,7 @@ def main(argv=None) -> int:
                             "down": seg_ms[2] * 1e3, "combine": seg_ms[3] * 1e3},
             "down_kernel_us": down_ms * 1e3,
             "down_GBps": work["down_bytes"] / (down_ms * 1e-3) / 1e9,
-            "down_traffic": counter_traffic(args.workload, "down"),
+            "down_traffic": counter_traffic(args.workload, "down") if counters_apply else None,
         },
     }
     if not args.no_cpu_baseline:
