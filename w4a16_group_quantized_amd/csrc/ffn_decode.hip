@@ -197,6 +197,7 @@ struct Geom {
   int nb;    // blocks per expert
   int nwg;   // workgroups (one per compute unit)
   int wmax;  // units per window (bounded by LDS)
+  int u32;   // nonzero when E * nb * nwg < 2^32: the shares in 32-bit arithmetic
 };
 
 constexpr int kXE = 2;  // experts per window
@@ -417,9 +418,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   auto offset_at = [&](int e) { if constexpr (NPL > 0) return roff[e]; else return p.offsets[e]; };
   auto sorted_at = [&](int r) { if constexpr (NPL > 0) return rsorted[r]; else return p.sorted_slots[r]; };
 
-  const int64_t U = static_cast<int64_t>(n_active) * nb;
-  const int u0 = static_cast<int>(U * blockIdx.x / geo.nwg);
-  const int u1 = static_cast<int>(U * (blockIdx.x + 1) / geo.nwg);
+  // This workgroup's share [u0, u1) of the units; in 32 bits when the
+  // products fit (a 64-bit division is a long instruction sequence that every
+  // wave runs before its first load).
+  int u0, u1;
+  if (geo.u32) {
+    const uint32_t U = static_cast<uint32_t>(n_active) * nb;
+    u0 = static_cast<int>(U * blockIdx.x / static_cast<uint32_t>(geo.nwg));
+    u1 = static_cast<int>(U * (blockIdx.x + 1) / static_cast<uint32_t>(geo.nwg));
+  } else {
+    const int64_t U = static_cast<int64_t>(n_active) * nb;
+    u0 = static_cast<int>(U * blockIdx.x / geo.nwg);
+    u1 = static_cast<int>(U * (blockIdx.x + 1) / geo.nwg);
+  }
 
   for (int w0 = u0; w0 < u1;) {
     const int a0 = w0 / nb;
@@ -429,8 +440,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
     // of the first pass are out (that pass needs none: every active expert
     // has a row)
     int xe[kXE], xr0[kXE] = {0, 0}, xrows[kXE] = {1, 1};
+    // both entries loaded together (a clamped index instead of a branch per
+    // entry, which waited for each load in turn)
 #pragma unroll
-    for (int i = 0; i < kXE; ++i) xe[i] = i < nx ? active_at(a0 + i) : 0;
+    for (int i = 0; i < kXE; ++i) xe[i] = active_at(min(a0 + i, n_active - 1));
+    __builtin_amdgcn_sched_barrier(0);  // both loads issued before either is used
+#pragma unroll
+    for (int i = 0; i < kXE; ++i) xe[i] = i < nx ? xe[i] : 0;
     int maxrows = 1;
     for (int c = 0; c < maxrows; c += NA) {
       if (w0 != u0 || c != 0) lds_barrier();  // the previous pass no longer reads LDS
@@ -696,8 +712,10 @@ void launch_decode_npl(const DecodeArgs& p, Geom geo, int na, size_t lds, hipStr
 // route: stage 1 routes the tokens itself (p.logits, p.E <= 1024, T <= 64).
 template <bool GATE_UP>
 void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream, bool route) {
+  // (p.E is set by every caller: the share arithmetic's width depends on it)
   const DeviceInfo dev = device_info();
   geo.nwg = dev.cus;
+  geo.u32 = static_cast<uint64_t>(p.E) * geo.nb * geo.nwg < (1ull << 32);
   const size_t rbytes = route ? route_lds_bytes(p.E, p.T * p.top_k) : 0;
   const int na = plan<GATE_UP>(geo, p.T, slots, dev, rbytes);
   const size_t lds = launch_lds<GATE_UP>(geo, na) + rbytes;
@@ -735,6 +753,7 @@ void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStrea
   p.top_k = a.top_k;
   p.H = a.H;
   p.I = a.I;
+  p.E = a.E;
   p.act_hi = ws.act_hi;
   p.act_lo = ws.act_lo;
   launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, false);
@@ -792,6 +811,7 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
   p.top_k = a.top_k;
   p.H = a.H;
   p.I = a.I;
+  p.E = a.E;
   p.y = a.y;
   launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream, false);
 }
