@@ -78,13 +78,53 @@ __global__ __launch_bounds__(256) void permute_mask_kernel(
 }
 
 // Scan over blocks (per expert, in place: counts become rows in earlier
-// blocks) and over experts (offsets, active list).
+// blocks) and over experts (offsets, active list).  With E <= kScanThreads
+// every expert's blocks are split over P = kScanThreads / E threads: each
+// scans its own range, the part totals meet in LDS, and a second pass adds
+// the earlier parts' totals (a few round trips however many blocks, instead
+// of one per 16 blocks and expert in turn).
 __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
     int nblocks, int S, int E, int* __restrict__ gcount, int* __restrict__ offsets,
     int* __restrict__ active, int* __restrict__ num_active) {
   __shared__ int wave_tot[kScanThreads / 64 + 1];
+  __shared__ int part_tot[kScanThreads];
   const int tid = threadIdx.x;
   int cnt[kPerThread], off[kPerThread];
+  if (E <= kScanThreads) {
+    const int P = kScanThreads / E;
+    const int e = tid % E, part = tid / E;
+    const int b0 = part < P ? nblocks * part / P : 0;
+    const int b1 = part < P ? nblocks * (part + 1) / P : 0;
+    int run = 0;
+    for (int bb = b0; bb < b1; bb += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = bb + u < b1 ? gcount[static_cast<size_t>(bb + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (bb + u < b1) gcount[static_cast<size_t>(bb + u) * E + e] = run;
+        run += c[u];
+      }
+    }
+    if (part < P) part_tot[part * E + e] = run;
+    __syncthreads();
+    if (part < P) {
+      int base = 0;
+      for (int q = 0; q < part; ++q) base += part_tot[q * E + e];
+      if (base != 0)
+        for (int bb = b0; bb < b1; ++bb) gcount[static_cast<size_t>(bb) * E + e] += base;
+    }
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int ee = kPerThread * tid + i;
+      int tot = 0;
+      if (ee < E)
+        for (int q = 0; q < P; ++q) tot += part_tot[q * E + ee];
+      cnt[i] = tot;
+    }
+    write_offsets_and_active(cnt, E, S, offsets, active, num_active, wave_tot, off);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const int e = kPerThread * tid + i;
