@@ -321,6 +321,26 @@ def main(argv=None) -> int:
     fused_eager_ms = t_start.elapsed_time(t_end) / args.steps
     log(f"eager moe_layer_forward: {fused_eager_ms * 1e3:.1f} us/step")
 
+    # Per-step spread of the same eager steps (events around each step), and a
+    # labelled hot-cache figure: every step on one weight copy, whose active
+    # experts then stay in the last-level cache (not a layer of a model).
+    def per_step_us(copy_of) -> np.ndarray:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            layer.forward(logits, x, copies[copy_of(i)])
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+
+    spread = per_step_us(lambda i: i % args.layers)
+    hot = per_step_us(lambda i: 0)
+    step_pct = {f"p{q}": float(np.percentile(spread, q)) for q in (10, 50, 90)}
+    log(f"eager steps p10/p50/p90 {step_pct['p10']:.1f} / {step_pct['p50']:.1f} / "
+        f"{step_pct['p90']:.1f} us; hot-cache (one weight copy) p50 {np.median(hot):.1f} us")
+
     # HIP graphs: one captured step per weight copy, replayed round-robin
     graph_ms = None
     if not args.no_graph:
@@ -397,6 +417,8 @@ def main(argv=None) -> int:
         "layer": {
             "eager_us_per_step": eager_ms * 1e3,
             "eager_layer_forward_us_per_step": fused_eager_ms * 1e3,
+            "eager_step_us_percentiles": step_pct,
+            "hot_cache_us_per_step_p50": float(np.median(hot)),
             "graph_us_per_step": graph_ms * 1e3 if graph_ms is not None else None,
             "algorithmic_bytes": work["layer_bytes"],
             "layer_GBps": work["layer_bytes"] / (ms * 1e-3) / 1e9,
