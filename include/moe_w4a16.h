@@ -20,9 +20,11 @@
  *     tensors are passed as uint16_t bit patterns.  Every non-null tensor
  *     pointer must be 16-byte aligned.  All tensors are dense, row-major.
  *   - Ownership: the caller allocates and frees every buffer, including the
- *     workspaces.  The library never allocates or frees memory, never
- *     synchronises, keeps no mutable global state and may be called from
- *     several host threads at once.
+ *     workspaces.  The library never allocates or frees memory and never
+ *     synchronises.  Its only host-side state is a per-device cache of two
+ *     device attributes (compute-unit count, LDS bytes per workgroup) read
+ *     from the runtime on first use; it may be called from several host
+ *     threads at once.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *     default stream) and runs asynchronously.  A call that returns MOE_OK has
  *     only enqueued its kernels.

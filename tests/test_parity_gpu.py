@@ -2,15 +2,22 @@
 
 Bit-exact: top-k ids, expert offsets, sorted slots, slot rows, active experts
 and their count.  Floating point: fp16 layer output within max |err| <= 2e-2
-and relative RMS <= 1e-2 of the unrounded fp64 oracle (tests/parity.py), the
-fp32 router weights within 1e-6, and the fp32 per-row expert outputs within a
-relative RMS of 1e-4.
+and relative RMS <= 1e-2 of the unrounded oracle (tests/parity.py), the fp32
+router weights within 1e-6, and every row of the fp32 per-row expert outputs
+y_sorted element by element (tests/parity.py states the bound).
 
-Sizes: every named workload (at its full size; the two prefill workloads are
-checked on sampled tokens, whose outputs the oracle computes one by one, plus
-bit-exact routing over all tokens), token counts 0/1/2/8/9/127/128, and the
-degenerate cases (one expert, k = E, E not a multiple of 64, every token on
-one expert, tied logits, the largest E and k).
+Every output buffer is filled with NaN (and every workspace with 0xFF bytes)
+before a call, so a row, tile or item the kernels never write fails the check
+instead of passing on stale memory.  Each layer is run both as the four
+separate calls and as the one-call moe_layer_forward, which must agree bit for
+bit.
+
+Sizes: every named workload at its full size (the two prefill workloads
+against the fp32 oracle, every token and every y_sorted row), token counts
+0/1/2/8/9/63/64/65/127/128, the 128-row M-tile path (S >= 64 E) with last
+tiles of 1 to 4 live 32-row subtiles, and the degenerate cases (one expert,
+k = E, E not a multiple of 64, every token on one expert, tied logits, the
+largest E and k).
 """
 
 from __future__ import annotations
@@ -19,7 +26,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.parity import assert_fp16_close
+from tests.parity import assert_fp16_close, assert_y_close
 from w4a16_group_quantized_amd import inputs as synth
 
 pytestmark = pytest.mark.gpu
@@ -43,14 +50,33 @@ def _announce(request):
     yield
 
 
+def _poison(layer):
+    """NaN in every output, 0xFF bytes in every workspace (sentinels)."""
+    nan = float("nan")
+    layer.y_sorted.fill_(nan)
+    layer.out.fill_(nan)
+    layer.fused_out.fill_(nan)
+    layer.weights.fill_(nan)
+    layer.ids.fill_(-7)
+    for v in layer.perm.values():
+        v.fill_(-7)
+    for ws in (layer.perm_ws, layer.ffn_ws, layer.layer_ws):
+        ws.fill_(255)
+
+
 def _run_layer(host, shape, dev):
+    """The layer as the four calls and as moe_layer_forward (bit-equal), on
+    poisoned buffers; returns the four calls' outputs as numpy arrays."""
     from w4a16_group_quantized_amd import ops
 
     w = ops.weights_to_device(host, dev)
     logits = torch.from_numpy(host["logits"]).to(dev)
     x = torch.from_numpy(host["x"]).to(dev)
     layer = ops.MoELayer(shape.T, shape.E, shape.top_k, shape.H, shape.I, dev)
+    _poison(layer)
+    torch.cuda.synchronize()
     out = layer(logits, x, w)
+    fused = layer.forward(logits, x, w)
     torch.cuda.synchronize()
     res = {
         "topk_ids": layer.ids.cpu().numpy(),
@@ -61,6 +87,12 @@ def _run_layer(host, shape, dev):
     for k, v in layer.perm.items():
         res[k] = v.cpu().numpy()
     res["num_active"] = int(res["num_active"][0])
+    if shape.T > 0:
+        assert torch.equal(fused.view(torch.int16), out.view(torch.int16)), \
+            "moe_layer_forward differs from the four calls"
+        views = layer.forward_views()
+        assert torch.equal(views["y_sorted"].view(torch.int32), layer.y_sorted.view(torch.int32))
+        assert torch.equal(views["topk_ids"], layer.ids)
     return res
 
 
@@ -72,17 +104,15 @@ def _assert_routing_exact(got, ref):
     assert got["num_active"] == int(ref["num_active"]), "num_active"
 
 
-def _full_check(shape, seed, dev, host=None):
+def _full_check(shape, seed, dev, host=None, dtype=np.float64):
     host = host if host is not None else synth.make_inputs(shape, seed)
-    ref = oracle.layer(host, shape.top_k)
+    ref = oracle.layer(host, shape.top_k, dtype=dtype)
     got = _run_layer(host, shape, dev)
     if shape.T == 0:  # nothing is computed or written; outputs are empty
         assert got["topk_ids"].shape == (0, shape.top_k) and got["out"].shape == (0, shape.H)
         return got, ref
     _assert_routing_exact(got, ref)
-    yref = ref["y_sorted"]
-    yerr = np.sqrt(((got["y_sorted"] - yref) ** 2).sum() / max((yref ** 2).sum(), 1e-30))
-    assert yerr < 1e-4, f"y_sorted rel-RMS {yerr}"
+    assert_y_close(got["y_sorted"], ref["y_sorted"], f"{shape} seed {seed}")
     assert_fp16_close(got["out"], ref["out"], f"{shape} seed {seed}")
     return got, ref
 
@@ -104,30 +134,79 @@ def test_decode_shard_token_sweep(dev, T):
     _full_check(synth.MoEShape(base.E, base.top_k, base.H, base.I, T), 0, dev)
 
 
-def _sampled_check(shape, dev, n_sample=40, seed=0):
-    host = synth.make_inputs(shape, seed)
-    ids, w = oracle.route(host["logits"], shape.top_k)
-    perm = oracle.permute(ids, shape.E)
-    got = _run_layer(host, shape, dev)
-    ref = {"topk_ids": ids, "topk_weights": w, **perm}
-    _assert_routing_exact(got, ref)
-    rng = np.random.default_rng(1234)
-    tokens = np.unique(np.concatenate([[0, shape.T - 1], rng.choice(shape.T, n_sample, replace=False)]))
-    sub = oracle.token_outputs(host, ids, w, tokens)
-    assert_fp16_close(got["out"][tokens], sub, f"{shape} sampled {tokens.size} tokens")
-    return got, host, ids
+def test_prefill_workload_full(dev):
+    """1024 tokens: every token and every y_sorted row against the fp32 oracle."""
+    _full_check(synth.WORKLOADS["prefill_e512_k10_h2560_i640_t1024"], 0, dev, dtype=np.float32)
 
 
-def test_prefill_workload_sampled(dev):
-    _sampled_check(synth.WORKLOADS["prefill_e512_k10_h2560_i640_t1024"], dev)
-
-
-def test_prefill_zipf_workload_sampled(dev):
+def test_prefill_zipf_workload_full(dev):
+    """4096 tokens with Zipf-skewed routing (the 128-row M-tile path): every
+    token and every y_sorted row against the fp32 oracle."""
     shape = synth.WORKLOADS["prefill_zipf_e512_k10_h2560_i640_t4096"]
-    got, host, ids = _sampled_check(shape, dev)
+    got, _ = _full_check(shape, 0, dev, dtype=np.float32)
     # the skew is real: the hottest expert holds hundreds of rows
     counts = np.diff(got["expert_offsets"])
     assert counts.max() > 1000 and (counts == 0).sum() > 100
+
+
+def test_layer_forward_decode_workload_against_oracle(dev):
+    """The timed decode step (moe_layer_forward, 8 tokens, model geometry,
+    seed 0) against the oracle directly, with its routing and y_sorted."""
+    from w4a16_group_quantized_amd import ops
+
+    shape = synth.WORKLOADS["decode_e512_k10_h2560_i640_t8"]
+    host = synth.make_inputs(shape, 0)
+    ref = oracle.layer(host, shape.top_k)
+    w = ops.weights_to_device(host, dev)
+    layer = ops.MoELayer(shape.T, shape.E, shape.top_k, shape.H, shape.I, dev)
+    _poison(layer)
+    out = layer.forward(torch.from_numpy(host["logits"]).to(dev),
+                        torch.from_numpy(host["x"]).to(dev), w)
+    torch.cuda.synchronize()
+    v = layer.forward_views()
+    got = {k: t.cpu().numpy() for k, t in v.items()}
+    got["num_active"] = int(got["num_active"][0])
+    _assert_routing_exact(got, ref)
+    assert_y_close(got["y_sorted"], ref["y_sorted"], "moe_layer_forward decode")
+    assert_fp16_close(out.cpu().numpy(), ref["out"], "moe_layer_forward decode")
+
+
+def _last_tile_subtiles(counts):
+    return {int(((c - 1) % 128) // 32 + 1) for c in counts if c > 0}
+
+
+@pytest.mark.parametrize("E,k,H,I,T", [
+    (8, 2, 256, 128, 256),    # S = 64 E exactly
+    (8, 2, 288, 96, 300),     # odd group counts (9 and 3): no wide scale/zero loads
+    (4, 2, 256, 128, 200),
+    (4, 2, 256, 128, 256),
+    (4, 2, 288, 96, 333),
+])
+def test_m128_tile_path_full(dev, E, k, H, I, T):
+    """S >= 64 E selects 128-row M-tiles; whole outputs against the oracle."""
+    shape = synth.MoEShape(E=E, top_k=k, H=H, I=I, T=T)
+    assert T * k >= 64 * E
+    got, _ = _full_check(shape, 5, dev)
+    print(f"  last-tile live subtiles {sorted(_last_tile_subtiles(np.diff(got['expert_offsets'])))}")
+
+
+def test_m128_tile_cases_cover_every_tail():
+    """The cases above end experts in last M-tiles of 1, 2, 3 and 4 live subtiles."""
+    seen = set()
+    for (E, k, H, I, T) in [(8, 2, 256, 128, 256), (8, 2, 288, 96, 300), (4, 2, 256, 128, 200),
+                            (4, 2, 256, 128, 256), (4, 2, 288, 96, 333)]:
+        h = synth.make_activations(synth.MoEShape(E=E, top_k=k, H=H, I=I, T=T), 5)
+        ids, _ = oracle.route(h["logits"], k)
+        seen |= _last_tile_subtiles(np.bincount(ids.ravel(), minlength=E))
+    assert seen == {1, 2, 3, 4}
+
+
+def test_skewed_small_prefill(dev):
+    """A few experts take most rows (many 128-row tiles), many take none."""
+    shape = synth.MoEShape(E=32, top_k=3, H=256, I=128, T=700, zipf_s=1.1)
+    got, _ = _full_check(shape, 4, dev)
+    counts = np.diff(got["expert_offsets"])
+    assert counts.max() > 256 and counts.min() < 32
 
 
 # --------------------------------------------------------------------------- #

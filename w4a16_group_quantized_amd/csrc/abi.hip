@@ -3,6 +3,8 @@
 // Nothing here allocates, frees or synchronises.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/moe_w4a16.h"
 #include "common.h"
 
@@ -47,6 +49,29 @@ int check_dims(int32_t H, int32_t I, int32_t group_size) {
 }  // namespace
 
 namespace moe {
+
+DeviceInfo device_info() {
+  static std::atomic<uint64_t> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const uint64_t v = cache[dev].load(std::memory_order_relaxed);
+    if (v) return {static_cast<int>(v >> 32), static_cast<int>(v & 0xFFFFFFFFu)};
+  }
+  int cus = 0, lds = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess ||
+      cus < 1)
+    cus = 256;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev < 0 ? 0 : dev) !=
+          hipSuccess ||
+      lds < 65536)
+    lds = 65536;
+  if (dev >= 0)
+    cache[dev].store((static_cast<uint64_t>(cus) << 32) | static_cast<uint32_t>(lds),
+                     std::memory_order_relaxed);
+  return {cus, lds};
+}
 
 // Layout: act_hi | act_lo | tile list | tile count | permuted x, each part
 // 256-byte aligned.  The tile list holds at most S + E entries (every tile

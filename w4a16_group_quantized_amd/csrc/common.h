@@ -5,8 +5,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
-
 namespace moe {
 
 constexpr int kGroup = 32;          // quantisation group size along K
@@ -15,6 +13,17 @@ constexpr int kMaxTopK = 64;        // top_k limit (one router round per lane)
 constexpr int kMaxGroups = 512;     // K / 32 limit (K <= 16384)
 constexpr int kPermBlockTokens = 64;  // tokens per permutation block (one 64-bit mask)
 constexpr int kDecodeMaxT = 8;      // T at or below which the GEMV variant runs
+constexpr int kMaxDevices = 64;     // devices with cached attributes
+
+// Compute-unit count and the LDS bytes one workgroup may use on the current
+// device.  Read from the runtime once per device and kept in a per-device
+// cache (a value never changes for a device, so threads racing on the cache
+// store the same thing).
+struct DeviceInfo {
+  int cus;
+  int lds;
+};
+DeviceInfo device_info();
 
 // ----------------------------------------------------------------------------
 // Launchers (each enqueues on `stream`, returns nothing; the ABI layer checks
@@ -103,51 +112,6 @@ void launch_down_prefill(const DownArgs& a, const FfnWorkspace& ws, hipStream_t 
 void launch_combine(const float* y_sorted, const float* weights,
                     const int* slot_rows, int T, int top_k, int H,
                     uint16_t* out, hipStream_t stream);
-
-// ----------------------------------------------------------------------------
-// Host helper: workgroups of `kernel` (launched with `threads` threads and
-// `lds` bytes of dynamic LDS) that the current device holds at once.  The
-// occupancy query costs host time, so results are cached in `table` (one
-// table per kernel, kCacheSlots entries per device, each entry
-// (lds + 1) << 32 | workgroups).  A value never changes for a given device,
-// kernel and LDS size, so two threads racing on an entry store the same thing.
-// ----------------------------------------------------------------------------
-constexpr int kMaxDevices = 64;   // devices with a cached occupancy figure
-constexpr int kCacheSlots = 8;
-using OccTable = std::atomic<uint64_t>[kMaxDevices * kCacheSlots];
-
-template <typename Kernel>
-int resident_workgroups(Kernel kernel, int threads, size_t lds, OccTable& table) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
-  const uint64_t key = static_cast<uint64_t>(lds + 1) << 32;
-  if (dev >= 0) {
-    for (int i = 0; i < kCacheSlots; ++i) {
-      const uint64_t v = table[dev * kCacheSlots + i].load(std::memory_order_relaxed);
-      if (v == 0) break;
-      if ((v & ~0xFFFFFFFFull) == key) return static_cast<int>(v & 0xFFFFFFFFull);
-    }
-  }
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
-          hipSuccess ||
-      cus < 1)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
-      per_cu < 1)
-    per_cu = 1;
-  const int resident = per_cu * cus;
-  if (dev >= 0) {
-    for (int i = 0; i < kCacheSlots; ++i) {
-      uint64_t expected = 0;
-      std::atomic<uint64_t>& slot = table[dev * kCacheSlots + i];
-      if (slot.compare_exchange_strong(expected, key | static_cast<uint32_t>(resident)) ||
-          (expected & ~0xFFFFFFFFull) == key)
-        break;
-    }
-  }
-  return resident;
-}
 
 // ----------------------------------------------------------------------------
 // Device helpers

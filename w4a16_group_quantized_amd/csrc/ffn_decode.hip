@@ -642,34 +642,6 @@ int cluster_lanes(int G) {
   return C;
 }
 
-struct DeviceInfo {
-  int cus;
-  int lds;
-};
-
-DeviceInfo device_info() {
-  static std::atomic<uint64_t> cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
-  if (dev >= 0) {
-    const uint64_t v = cache[dev].load(std::memory_order_relaxed);
-    if (v) return {static_cast<int>(v >> 32), static_cast<int>(v & 0xFFFFFFFFu)};
-  }
-  int cus = 0, lds = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
-          hipSuccess ||
-      cus < 1)
-    cus = 256;
-  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev < 0 ? 0 : dev) !=
-          hipSuccess ||
-      lds < 65536)
-    lds = 65536;
-  if (dev >= 0)
-    cache[dev].store((static_cast<uint64_t>(cus) << 32) | static_cast<uint32_t>(lds),
-                     std::memory_order_relaxed);
-  return {cus, lds};
-}
-
 // LDS bytes of the A fragments: kXE experts x na rows (stage 2: hi and lo).
 template <bool GATE_UP>
 size_t frag_bytes(const Geom& geo, int na) {

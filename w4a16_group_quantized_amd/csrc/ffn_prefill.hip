@@ -136,59 +136,62 @@ struct BRegs {
 
 struct BAddr {
   __amdgpu_buffer_rsrc_t rq, rs, rz;
-  uint32_t q_row, s_row, z_row;       // byte offsets of the lane's row (q_row: plus h * 16)
+  uint32_t q_row, s_row, z_row;       // byte offsets of the first group of the lane's row
   uint32_t q_oob, s_oob, z_oob;       // offsets that read as zero
   int G;
   int h;                              // lane half
 };
 
-// Loads of one stage's weight operands.  The lane's row is in the vector
-// offset and the group in the scalar offset, clamped to the matrix: a stage
-// past the end re-reads valid data that the compute skips, and a lane past
-// the matrix reads from the end of the buffers (zeros).  No branches and no
-// vector arithmetic, so the wait counts after the loads are exact.  VEC (the
-// group count is a multiple of kKC): a stage's zero words and scales of one
-// row are contiguous and aligned, and are read with one wide load each.
+// Loads of one stage's weight operands.  The whole byte offset of every load
+// is in the vector offset (the scalar offset is 0), so the buffer's range
+// check covers the full address: a lane past the matrix reads at or beyond
+// the end of the buffer and gets zeros without touching memory.  Groups are
+// clamped to the lane's own row: a stage past the end of K re-reads the row's
+// last valid groups, which the compute skips.  VEC (the group count is a
+// multiple of kKC): a stage's zero words and scales of one row are contiguous
+// and aligned, and are read with one wide load each.
 template <int KC, bool VEC>
 __device__ __forceinline__ void load_b_stage(const BAddr& ba, int g0, BRegs<KC>& b) {
 #pragma unroll
   for (int pp = 0; pp < KC / 2; ++pp) {
-    // lane half h loads group g0 + 2 pp + h: ba.q_row already holds h * 16
-    const int g = min(g0 + 2 * pp, ba.G - 1);
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rq, static_cast<int>(ba.q_row), g * 16, 0);
+    // lane half h loads group g0 + 2 pp + h of its own row (ba.q_row is the
+    // row's first byte)
+    const uint32_t g = static_cast<uint32_t>(min(g0 + 2 * pp + ba.h, ba.G - 1));
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rq, static_cast<int>(ba.q_row + g * 16u), 0, 0);
     b.q[pp] = make_uint4(v[0], v[1], v[2], v[3]);
   }
   if constexpr (VEC) {
-    const int gs = min(g0, ba.G - KC);
-    const int zo = static_cast<int>(ba.z_row), so = static_cast<int>(ba.s_row);
+    const uint32_t gs = static_cast<uint32_t>(min(g0, ba.G - KC));
     if constexpr (KC == 2) {
-      const auto z = __builtin_amdgcn_raw_buffer_load_b64(ba.rz, zo, gs * 4, 0);
+      const auto z = __builtin_amdgcn_raw_buffer_load_b64(ba.rz, static_cast<int>(ba.z_row + gs * 4u), 0, 0);
       b.z[0] = z[0];
       b.z[1] = z[1];
     } else {
 #pragma unroll
       for (int i = 0; i < KC; i += 4) {
-        const auto z = __builtin_amdgcn_raw_buffer_load_b128(ba.rz, zo, (gs + i) * 4, 0);
+        const auto z = __builtin_amdgcn_raw_buffer_load_b128(
+            ba.rz, static_cast<int>(ba.z_row + (gs + i) * 4u), 0, 0);
         for (int t = 0; t < 4; ++t) b.z[i + t] = z[t];
       }
     }
+    const int so = static_cast<int>(ba.s_row + gs * 2u);
     if constexpr (KC == 8) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rs, so, gs * 2, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rs, so, 0, 0);
       for (int t = 0; t < 4; ++t) b.s[t] = v[t];
     } else if constexpr (KC == 4) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ba.rs, so, gs * 2, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ba.rs, so, 0, 0);
       b.s[0] = v[0];
       b.s[1] = v[1];
     } else {
-      b.s[0] = __builtin_amdgcn_raw_buffer_load_b32(ba.rs, so, gs * 2, 0);
+      b.s[0] = __builtin_amdgcn_raw_buffer_load_b32(ba.rs, so, 0, 0);
     }
   } else {
     uint32_t sv[KC];
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
-      const int g = min(g0 + i, ba.G - 1);
-      b.z[i] = __builtin_amdgcn_raw_buffer_load_b32(ba.rz, static_cast<int>(ba.z_row), g * 4, 0);
-      sv[i] = __builtin_amdgcn_raw_buffer_load_b16(ba.rs, static_cast<int>(ba.s_row), g * 2, 0);
+      const uint32_t g = static_cast<uint32_t>(min(g0 + i, ba.G - 1));
+      b.z[i] = __builtin_amdgcn_raw_buffer_load_b32(ba.rz, static_cast<int>(ba.z_row + g * 4u), 0, 0);
+      sv[i] = __builtin_amdgcn_raw_buffer_load_b16(ba.rs, static_cast<int>(ba.s_row + g * 2u), 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < KC; i += 2) b.s[i / 2] = sv[i] | (i + 1 < KC ? sv[i + 1] << 16 : 0u);
@@ -224,11 +227,15 @@ struct ASrc {
 // groups, while the 8 lanes of any aligned octet still read distinct ones.
 __device__ __forceinline__ int slot_xor(int g, int h, int t) { return ((g & 1) << 2) | (h << 1) | t; }
 
+// The whole byte offset is in the vector offset, and a group past the end of
+// K is clamped to the row's last group (the compute skips it), so every load
+// stays inside the row it stages; rows past the tile start at or beyond the
+// end of the buffer and read zeros.
 template <bool GATE_UP, int MSUB, int NS>
-__device__ __forceinline__ void load_a(uint32_t tid, const ASrc& src, int g0, AStage<GATE_UP, MSUB>& a) {
+__device__ __forceinline__ void load_a(uint32_t tid, const ASrc& src, int g0, int G,
+                                       AStage<GATE_UP, MSUB>& a) {
   using S = AStage<GATE_UP, MSUB>;
   const int t8 = static_cast<int>(tid % S::kTPR);
-  const int soff = g0 * kGroup * 2;
 #pragma unroll
   for (int i = 0; i < NS; ++i)
 #pragma unroll
@@ -237,8 +244,9 @@ __device__ __forceinline__ void load_a(uint32_t tid, const ASrc& src, int g0, AS
       const int cp = cc / (S::kKC * 4);
       const int g = (cc / 4) % S::kKC;
       const int c = cc % 4;
+      const uint32_t ga = static_cast<uint32_t>(min(g0 + g, G - 1));
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(
-          src.r[cp], static_cast<int>(src.row_off[i] + g * kGroup * 2 + c * 16), soff, 0);
+          src.r[cp], static_cast<int>(src.row_off[i] + ga * (kGroup * 2) + c * 16), 0, 0);
       a.v[i][k] = make_uint4(v[0], v[1], v[2], v[3]);
     }
 }
@@ -347,7 +355,7 @@ __device__ __forceinline__ void main_loop(uint32_t tid, const ASrc& asrc, uint16
   BRegs<KC> bcur, bnxt;
   AStage<GATE_UP, MSUB> astage;
   load_b_stage<KC, VEC>(ba, 0, bcur);
-  load_a<GATE_UP, MSUB, NS>(tid, asrc, 0, astage);
+  load_a<GATE_UP, MSUB, NS>(tid, asrc, 0, G, astage);
   store_a<GATE_UP, MSUB, NS>(tid, astage, lds);
   __syncthreads();
   for (int s = 0; s < nfull; ++s) {
@@ -355,7 +363,7 @@ __device__ __forceinline__ void main_loop(uint32_t tid, const ASrc& asrc, uint16
     // The next stage's loads are issued unconditionally (past the end of K
     // they read zeros or the following row), so every wait below is exact.
     load_b_stage<KC, VEC>(ba, g0 + KC, bnxt);
-    load_a<GATE_UP, MSUB, NS>(tid, asrc, g0 + KC, astage);
+    load_a<GATE_UP, MSUB, NS>(tid, asrc, g0 + KC, G, astage);
     // keep the loads ahead of the compute that hides their latency
     __builtin_amdgcn_sched_barrier(0);
     compute_stage<GATE_UP, MSUB, NS, KC>(tid, lds + (s & 1) * S::kStageHalfs, bcur, zshift, bias,
@@ -434,7 +442,7 @@ __device__ __forceinline__ void process_item(const PrefillArgs& p, int slot, int
   ba.s_oob = static_cast<uint32_t>(N) * G * 2u;
   ba.z_oob = static_cast<uint32_t>(N / 8) * G * 4u;
   // a lane past the matrix reads from the end of the buffers: zeros
-  ba.q_row = n_ok ? static_cast<uint32_t>(n) * G * 16u + h * 16u : ba.q_oob;
+  ba.q_row = n_ok ? static_cast<uint32_t>(n) * G * 16u : ba.q_oob;
   ba.s_row = n_ok ? static_cast<uint32_t>(n) * G * 2u : ba.s_oob;
   ba.z_row = n_ok ? static_cast<uint32_t>(n >> 3) * G * 4u : ba.z_oob;
   const uint32_t zshift = 4u * static_cast<uint32_t>(n & 7);
