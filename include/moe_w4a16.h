@@ -21,10 +21,12 @@
  *     pointer must be 16-byte aligned.  All tensors are dense, row-major.
  *   - Ownership: the caller allocates and frees every buffer, including the
  *     workspaces.  The library never allocates or frees memory and never
- *     synchronises.  Its only host-side state is a per-device cache of two
- *     device attributes (compute-unit count, LDS bytes per workgroup) read
- *     from the runtime on first use; it may be called from several host
- *     threads at once.
+ *     synchronises.  Its only state is a per-device cache of two device
+ *     attributes (compute-unit count, LDS bytes per workgroup) read from the
+ *     runtime on first use, and the per-device scratch array of
+ *     moe_layer_forward_noalloc with its address cache.  Entry points other
+ *     than moe_layer_forward_noalloc may be called from several host threads
+ *     at once.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *     default stream) and runs asynchronously.  A call that returns MOE_OK has
  *     only enqueued its kernels.
@@ -268,6 +270,41 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T,
                       const int32_t* w2_qzeros, int32_t H, int32_t I,
                       int32_t group_size, uint16_t* out, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* Scratch bytes of moe_layer_forward_noalloc (per device). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * moe_layer_forward_noalloc - moe_layer_forward for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same layer on
+ * the same kernels, with the workspace taken from a scratch array that the
+ * library holds on every device it runs on (MOE_NOALLOC_SCRATCH_BYTES, from
+ * module load to process end).  out is what moe_layer_forward returns, bit
+ * for bit.  The call allocates nothing (no hipMalloc/hipFree, no allocating
+ * library routine); on its first call on a device it looks up that device's
+ * scratch address once.
+ *
+ *   arguments   as moe_layer_forward, without workspace / workspace_bytes
+ *
+ * Errors as moe_layer_forward; MOE_ERR_WORKSPACE when moe_layer_workspace_bytes
+ * for these sizes exceeds MOE_NOALLOC_SCRATCH_BYTES (at the 512-expert,
+ * top-10, H 2560, I 640 geometry that is above about 240 tokens), and
+ * MOE_ERR_HIP when the scratch address cannot be looked up; nothing is
+ * enqueued then.  Every call on one device shares that device's scratch:
+ * calls that overlap in time on one device (other streams, other threads)
+ * race and must not be issued.  The scratch keeps the last call's contents;
+ * a call reads nothing from it that it did not write itself.
+ */
+int moe_layer_forward_noalloc(const float* logits, const uint16_t* x, int64_t T,
+                              int32_t E, int32_t top_k,
+                              const int32_t* w13_qweight,
+                              const uint16_t* w13_scales,
+                              const int32_t* w13_qzeros,
+                              const int32_t* w2_qweight,
+                              const uint16_t* w2_scales,
+                              const int32_t* w2_qzeros, int32_t H, int32_t I,
+                              int32_t group_size, uint16_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -338,12 +338,12 @@ size_t moe_layer_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H,
   return layer_ws(nullptr, T, top_k, E, H, I).total;
 }
 
-int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t E, int32_t top_k,
-                      const int32_t* w13_qweight, const uint16_t* w13_scales,
-                      const int32_t* w13_qzeros, const int32_t* w2_qweight,
-                      const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t H, int32_t I,
-                      int32_t group_size, uint16_t* out, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+static int layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t E,
+                         int32_t top_k, const int32_t* w13_qweight, const uint16_t* w13_scales,
+                         const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                         const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t H, int32_t I,
+                         int32_t group_size, uint16_t* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   if (int st = check_routing(T, top_k, E)) return st;
   if (int st = check_dims(H, I, group_size)) return st;
   if (int st = check_prefill(T, top_k, E, H, I)) return st;
@@ -398,4 +398,68 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t
   return check_launch();
 }
 
+int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t E, int32_t top_k,
+                      const int32_t* w13_qweight, const uint16_t* w13_scales,
+                      const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                      const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t H, int32_t I,
+                      int32_t group_size, uint16_t* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return layer_forward(logits, x, T, E, top_k, w13_qweight, w13_scales, w13_qzeros, w2_qweight,
+                       w2_scales, w2_qzeros, H, I, group_size, out, workspace, workspace_bytes,
+                       stream);
+}
+
 }  // extern "C"
+
+// ---- the whole layer without a workspace argument ----------------------------
+// The scratch of moe_layer_forward_noalloc: one array per device, held from
+// module load to process end.  In host code `scratch` only names the symbol;
+// its device address (different on every device) comes from
+// hipGetSymbolAddress with that device current, and only that address is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void*> scratch_ptr[moe::kMaxDevices];
+
+// The current device's address of `scratch` (looked up once per device), or
+// nullptr with *err set when the runtime call fails.
+void* device_scratch(int* err) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= moe::kMaxDevices) {
+    *err = MOE_ERR_HIP;
+    return nullptr;
+  }
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      *err = MOE_ERR_HIP;
+      return nullptr;
+    }
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" int moe_layer_forward_noalloc(const float* logits, const uint16_t* x, int64_t T,
+                                         int32_t E, int32_t top_k, const int32_t* w13_qweight,
+                                         const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                                         const int32_t* w2_qweight, const uint16_t* w2_scales,
+                                         const int32_t* w2_qzeros, int32_t H, int32_t I,
+                                         int32_t group_size, uint16_t* out, void* stream) {
+  // sizes first: nothing is looked up or enqueued for a call that cannot run
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (int st = check_dims(H, I, group_size)) return st;
+  if (T == 0) return MOE_OK;
+  if (layer_ws(nullptr, T, top_k, E, H, I).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  int err = MOE_OK;
+  void* ws = device_scratch(&err);
+  if (ws == nullptr) return err;
+  return layer_forward(logits, x, T, E, top_k, w13_qweight, w13_scales, w13_qzeros, w2_qweight,
+                       w2_scales, w2_qzeros, H, I, group_size, out, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                       stream);
+}

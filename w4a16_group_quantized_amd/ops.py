@@ -39,7 +39,10 @@ EXPORTED = (
     "moe_combine",
     "moe_layer_workspace_bytes",
     "moe_layer_forward",
+    "moe_layer_forward_noalloc",
 )
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class MoEError(RuntimeError):
@@ -82,6 +85,9 @@ _SIGNATURES = {
     "moe_layer_forward": (
         ctypes.c_int,
         [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "moe_layer_forward_noalloc": (
+        ctypes.c_int,
+        [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P]),
 }
 
 
@@ -313,6 +319,20 @@ def moe_layer_forward(logits: torch.Tensor, x: torch.Tensor, top_k: int, w: dict
         _ptr(logits), _ptr(x), T, E, top_k, _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w13_z"]),
         _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]), H, I, GROUP_SIZE, _ptr(out),
         _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def moe_layer_forward_noalloc(logits: torch.Tensor, x: torch.Tensor, top_k: int, w: dict,
+                              out: torch.Tensor) -> torch.Tensor:
+    """moe_layer_forward without a workspace: the library's per-device scratch is used.
+    `out` fp16 [T, H] is the caller's (this call allocates nothing)."""
+    lib = load_library()
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w["w2_q"].shape[2] * 8
+    _check("moe_layer_forward_noalloc", lib.moe_layer_forward_noalloc(
+        _ptr(logits), _ptr(x), T, E, top_k, _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w13_z"]),
+        _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]), H, I, GROUP_SIZE, _ptr(out), _stream()))
     return out
 
 
