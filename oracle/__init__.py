@@ -7,13 +7,17 @@ no code with the HIP library and never imports it.
 
 from .moe_oracle import (  # noqa: F401
     GROUP_SIZE,
+    block,
     combine,
     dequantize,
     expert_ffn,
     grouped_ffn,
     layer,
+    layer_with_shared,
     permute,
     route,
+    router_logits,
+    shared_expert,
     silu,
     token_outputs,
     unpack_weight_codes,

@@ -26,6 +26,18 @@ Precision: every floating-point step runs in ``dtype`` (fp64 by default; fp32
 gives the "fp32 matmuls" variant).  Top-k ranks the fp32 logits themselves, so
 the selection is the same in any dtype.
 
+Around the routed layer (the MoE block): the router's gate projection makes
+the logits from the activations, logits = x @ Wg^T, and a shared expert (one
+more SwiGLU expert, in the same W4A16 format) runs on every token; its output
+is added to the routed output before the one rounding to fp16.  The pages name
+both only as the work beside the routed layer ("[Perf][SM70] Narrow Qwen3.8 AWQ
+active grouped decode", sections "New-base bounded integration acceptance
+(r2)", where the shared overlap is switched off, and "Capacity, startup, and
+remaining limit", which names the shared projection costs); they give no
+formula, so these are the plainest readings: an unquantised fp16 Wg [E, H]
+without bias, fp32 logits, and a shared expert with weight 1 and no gate of
+its own, stored as expert E after the E routed experts.
+
 Readings of points the pages leave open (listed with reasons in the design
 notes): weights are packed 8 per int32 along K, low nibble first, no column
 interleave; zeros are packed 8 per int32 along N; w13 rows [0, I) are gate and
@@ -226,3 +238,55 @@ def token_outputs(inputs: dict, ids: np.ndarray, weights: np.ndarray, tokens,
             w13, w2 = cache[e]
             out[i] += dtype(weights[t, j]) * expert_ffn(xt, w13, w2)[0]
     return out
+
+
+# --------------------------------------------------------------------------- #
+# the MoE block: router gate projection in front, shared expert beside
+# --------------------------------------------------------------------------- #
+_WEIGHT_KEYS = ("w13_q", "w13_z", "w13_s", "w2_q", "w2_z", "w2_s")
+
+
+def router_logits(x: np.ndarray, gate_weight: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """logits[t, e] = sum_h x[t, h] * Wg[e, h], for x [T, H] and Wg [E, H] (fp16 values)."""
+    return x.astype(dtype) @ gate_weight.astype(dtype).T
+
+
+def shared_expert(x: np.ndarray, weights: dict, dtype=np.float64) -> np.ndarray:
+    """The shared expert's FFN on every token: y [T, H].  It is the last expert
+    (index E) of weight arrays that hold E + 1 experts."""
+    e = weights["w13_q"].shape[0] - 1
+    w13 = dequantize(weights["w13_q"][e], weights["w13_z"][e], weights["w13_s"][e], dtype)
+    w2 = dequantize(weights["w2_q"][e], weights["w2_z"][e], weights["w2_s"][e], dtype)
+    return expert_ffn(x.astype(dtype), w13, w2)
+
+
+def layer_with_shared(inputs: dict, top_k: int, dtype=np.float64) -> dict:
+    """The routed layer over experts [0, E) (E from the logits) plus the shared
+    expert E: out = routed out + shared y, then one rounding to fp16."""
+    E = inputs["logits"].shape[1]
+    routed = layer({"logits": inputs["logits"], "x": inputs["x"],
+                    **{k: inputs[k][:E] for k in _WEIGHT_KEYS}}, top_k, dtype)
+    y_shared = shared_expert(inputs["x"], inputs, dtype)
+    out = routed["out"] + y_shared
+    res = dict(routed)
+    res.update({"routed_out": routed["out"], "y_shared": y_shared, "out": out,
+                "out_fp16": out.astype(np.float16)})
+    return res
+
+
+def block(inputs: dict, top_k: int, shared: bool = True, dtype=np.float64) -> dict:
+    """The MoE block: logits = router_logits(x, gate_w), rounded to fp32 (the
+    router ranks fp32 logits), then the routed layer, plus the shared expert
+    when ``shared``.  ``logits`` in the result is the fp32 array routed on and
+    ``logits_exact`` the projection before that rounding."""
+    exact = router_logits(inputs["x"], inputs["gate_w"], dtype)
+    logits = exact.astype(np.float32)
+    E = logits.shape[1]
+    inner = {"logits": logits, "x": inputs["x"], **{k: inputs[k] for k in _WEIGHT_KEYS}}
+    if shared:
+        res = layer_with_shared(inner, top_k, dtype)
+    else:
+        res = layer({**inner, **{k: inputs[k][:E] for k in _WEIGHT_KEYS}}, top_k, dtype)
+    res["logits"] = logits
+    res["logits_exact"] = exact
+    return res

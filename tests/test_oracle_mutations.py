@@ -14,7 +14,7 @@ from tests.conftest import GOLDEN
 
 _orig = {name: getattr(mo, name) for name in
          ("unpack_weight_codes", "unpack_zero_codes", "dequantize", "route", "permute",
-          "expert_ffn", "combine", "silu")}
+          "expert_ffn", "combine", "silu", "router_logits", "shared_expert")}
 
 
 def _unpack_high_first(qweight):
@@ -92,6 +92,32 @@ def _combine_wrong_rows(y_sorted, w, slot_rows):
     return out
 
 
+def _logits_gate_as_h_by_e(x, gate_weight, dtype=np.float64):
+    E, H = gate_weight.shape
+    return x.astype(dtype) @ gate_weight.reshape(H, E).astype(dtype)  # Wg read as [H, E]
+
+
+def _logits_drop_last_column(x, gate_weight, dtype=np.float64):
+    return x[:, :-1].astype(dtype) @ gate_weight[:, :-1].astype(dtype).T
+
+
+def _logits_fp16_sum(x, gate_weight, dtype=np.float64):
+    return (x @ gate_weight.T).astype(dtype)  # accumulated in fp16
+
+
+def _shared_half_weight(x, weights, dtype=np.float64):
+    return 0.5 * _orig["shared_expert"](x, weights, dtype)
+
+
+def _shared_first_expert(x, weights, dtype=np.float64):
+    first = {k: v[:1] for k, v in weights.items() if k.startswith("w")}
+    return _orig["shared_expert"](x, first, dtype)
+
+
+def _shared_dropped(x, weights, dtype=np.float64):
+    return np.zeros_like(_orig["shared_expert"](x, weights, dtype))
+
+
 MUTATIONS = {
     "nibbles high first": {"unpack_weight_codes": _unpack_high_first},
     "zero rows reversed": {"unpack_zero_codes": _zeros_along_k},
@@ -104,6 +130,12 @@ MUTATIONS = {
     "ties to higher index": {"route": _route_ties_high},
     "unstable segments": {"permute": _permute_unstable},
     "combine by slot not row": {"combine": _combine_wrong_rows},
+    "gate projection read as [H, E]": {"router_logits": _logits_gate_as_h_by_e},
+    "gate projection drops a column": {"router_logits": _logits_drop_last_column},
+    "gate projection summed in fp16": {"router_logits": _logits_fp16_sum},
+    "shared expert weight 1/2": {"shared_expert": _shared_half_weight},
+    "shared expert taken from expert 0": {"shared_expert": _shared_first_expert},
+    "shared expert dropped": {"shared_expert": _shared_dropped},
 }
 
 PINS = [
@@ -119,6 +151,10 @@ PINS = [
     pins.test_layer_gate_up_order_closed_form,
     pins.test_layer_matches_scalar_brute_force,
     pins.test_combine_gathers_by_slot_rows,
+    pins.test_router_logits_one_hot_closed_form,
+    pins.test_router_logits_match_exact_sums,
+    pins.test_shared_expert_closed_form,
+    pins.test_block_matches_scalar_brute_force,
 ]
 
 

@@ -335,3 +335,130 @@ def test_token_outputs_match_layer():
     res = oracle.layer(inp, shape.top_k)
     sub = oracle.token_outputs(inp, res["topk_ids"], res["topk_weights"], [0, 4, 8])
     np.testing.assert_allclose(sub, res["out"][[0, 4, 8]], rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- #
+# the MoE block: router gate projection and shared expert
+# --------------------------------------------------------------------------- #
+def test_router_logits_one_hot_closed_form():
+    """Row e of Wg holds c_e at column h(e) only, so logits[t, e] = c_e * x[t, h(e)] exactly."""
+    T, E, H = 3, 6, 32
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    h_of = [(5 * e + 3) % H for e in range(E)]
+    c = [2.0 ** (e - 2) for e in range(E)]
+    Wg = np.zeros((E, H), dtype=np.float16)
+    for e in range(E):
+        Wg[e, h_of[e]] = c[e]
+    L = oracle.router_logits(x, Wg)
+    assert L.shape == (T, E)
+    for t in range(T):
+        for e in range(E):
+            assert L[t, e] == c[e] * float(x[t, h_of[e]]), (t, e)
+
+
+def test_router_logits_match_exact_sums():
+    """fp16 x fp16 products are exact in fp64; math.fsum rounds their sum once."""
+    T, E, H = 3, 5, 96
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    Wg = (rng.standard_normal((E, H)) / np.sqrt(H)).astype(np.float16)
+    L = oracle.router_logits(x, Wg)
+    for t in range(T):
+        for e in range(E):
+            terms = [float(x[t, h]) * float(Wg[e, h]) for h in range(H)]
+            scale = math.fsum(abs(v) for v in terms)
+            assert abs(L[t, e] - math.fsum(terms)) <= 1e-13 * scale, (t, e)
+
+
+def _closed_form_expert(gate, up, H, I):
+    """Codes of one expert whose gate/up pre-activations are `gate` and `up` for
+    x = e_0 (each a (code, zero, scale) triple on column 0) and whose down
+    weights are all (9 - 8) / 16."""
+    c13 = np.zeros((2 * I, H), dtype=np.int64)
+    z13 = np.zeros((2 * I, H // 32), dtype=np.int64)
+    s13 = np.zeros((2 * I, H // 32), dtype=np.float16)
+    for rows, (code, zero, scale) in ((slice(0, I), gate), (slice(I, 2 * I), up)):
+        c13[rows, 0] = code
+        z13[rows, 0] = zero
+        s13[rows, 0] = scale
+    c2 = np.full((H, I), 9, dtype=np.int64)
+    z2 = np.full((H, I // 32), 8, dtype=np.int64)
+    s2 = np.full((H, I // 32), 1.0 / 16, dtype=np.float16)
+    return {"w13_q": _pack_rows(c13), "w13_z": _pack_zero_rows(z13), "w13_s": s13,
+            "w2_q": _pack_rows(c2), "w2_z": _pack_zero_rows(z2), "w2_s": s2}
+
+
+def test_shared_expert_closed_form():
+    """Three identical routed experts (gate 2, up 1) and a shared expert (gate -1,
+    up 2), x = e_0: out = I/16 * (SiLU(2) * 1 + SiLU(-1) * 2) for every h, since
+    the routed weights sum to 1 and the shared expert has weight 1."""
+    H, I, E, k = 32, 32, 3, 2
+    routed = _closed_form_expert((5, 1, 0.5), (5, 1, 0.25), H, I)   # (5-1)*.5 = 2, (5-1)*.25 = 1
+    shared = _closed_form_expert((2, 4, 0.5), (5, 1, 0.5), H, I)    # (2-4)*.5 = -1, (5-1)*.5 = 2
+    inp = {key: np.stack([routed[key]] * E + [shared[key]]) for key in routed}
+    x = np.zeros((2, H), dtype=np.float16)
+    x[:, 0] = 1.0
+    inp.update({"x": x, "logits": np.array([[0.5, -1.0, 2.0], [0.0, 0.0, 0.0]], np.float32)})
+    res = oracle.layer_with_shared(inp, k)
+
+    def silu(v):
+        return v / (1.0 + math.exp(-v))
+
+    expect = I / 16 * (silu(2.0) * 1.0 + silu(-1.0) * 2.0)
+    assert np.allclose(res["out"], expect, rtol=1e-13, atol=0)
+    assert np.allclose(res["y_shared"], I / 16 * silu(-1.0) * 2.0, rtol=1e-13, atol=0)
+
+
+def _brute_force_block(inp, top_k):
+    """Scalar restatement of the block: exact logits (fsum), rounded to fp32,
+    the routed layer's scalar loops, plus the shared expert's."""
+    x, Wg = inp["x"], inp["gate_w"]
+    T, H = x.shape
+    E = Wg.shape[0]
+    L = np.zeros((T, E), dtype=np.float32)
+    for t in range(T):
+        for e in range(E):
+            L[t, e] = np.float32(math.fsum(float(x[t, h]) * float(Wg[e, h]) for h in range(H)))
+    ids, w, out = _brute_force_layer({**inp, "logits": L}, top_k)
+    I = inp["w2_q"].shape[2] * 8
+
+    def wgt(which, n, kk):
+        q, z, s = inp[which + "_q"][E], inp[which + "_z"][E], inp[which + "_s"][E]
+        code = (int(q[n, kk // 8]) >> (4 * (kk % 8))) & 0xF
+        zero = (int(z[n // 8, kk // 32]) >> (4 * (n % 8))) & 0xF
+        return (code - zero) * float(s[n, kk // 32])
+
+    for t in range(T):
+        xt = [float(v) for v in x[t]]
+        h = [sum(xt[kk] * wgt("w13", n, kk) for kk in range(H)) for n in range(2 * I)]
+        a = [h[i] / (1.0 + math.exp(-h[i])) * h[I + i] for i in range(I)]
+        for hh in range(H):
+            out[t][hh] += sum(a[i] * wgt("w2", hh, i) for i in range(I))
+    return L, ids, w, out
+
+
+def test_block_matches_scalar_brute_force():
+    shape = synth.MoEShape(E=4, top_k=2, H=64, I=32, T=3)
+    inp = synth.make_block_inputs(shape, seed=5)
+    L, ids, w, out = _brute_force_block(inp, shape.top_k)
+    res = oracle.block(inp, shape.top_k)
+    assert np.array_equal(res["logits"], L)
+    assert np.array_equal(res["topk_ids"], ids)
+    np.testing.assert_allclose(res["topk_weights"], w, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(res["out"], out, rtol=1e-9, atol=1e-9)
+
+
+def test_shared_expert_alone_is_the_single_expert_layer():
+    """With every routed down scale zero the block is the shared expert alone,
+    which is the one-expert top-1 layer over the shared expert's weights."""
+    shape = synth.MoEShape(E=6, top_k=2, H=128, I=64, T=5)
+    inp = synth.make_block_inputs(shape, seed=6)
+    inp["w2_s"] = inp["w2_s"].copy()
+    inp["w2_s"][: shape.E] = 0
+    res = oracle.block(inp, shape.top_k)
+    single = oracle.layer({"logits": np.zeros((shape.T, 1), np.float32), "x": inp["x"],
+                           **{key: inp[key][shape.E:] for key in
+                              ("w13_q", "w13_z", "w13_s", "w2_q", "w2_z", "w2_s")}}, 1)
+    assert np.all(res["routed_out"] == 0.0)
+    np.testing.assert_allclose(res["out"], single["out"], rtol=1e-13, atol=1e-13)

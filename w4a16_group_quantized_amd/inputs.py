@@ -26,9 +26,16 @@ Tensor layouts (N = output rows, K = reduction dim, G = K / 32):
 Weight nibble j of a word is bits [4j, 4j+4) and holds k = 8*word + j; zero
 nibble j of a word holds row n = 8*word + j of that group.
 
-Draw order: ``SeedSequence(seed).spawn(8)`` gives one PCG64 stream per tensor,
-in the order logits, x, w13_q, w13_z, w13_s, w2_q, w2_z, w2_s.  Logits and x are
-filled row-major, so a smaller T is a row prefix of a larger T at the same seed.
+Draw order: ``SeedSequence(seed).spawn(9)`` gives one PCG64 stream per tensor,
+in the order logits, x, w13_q, w13_z, w13_s, w2_q, w2_z, w2_s, gate_w.  Every
+tensor is filled row-major, so a smaller T is a row prefix of a larger T at the
+same seed, and the weights of E + 1 experts are those of E experts followed by
+one more.
+
+The MoE block around the routed layer adds two inputs: the router's gate
+projection gate_w float16 [E, H], drawn N(0, 1/H) so that the logits it makes
+from N(0, 1) activations have unit variance like the logits drawn directly;
+and a shared expert, stored as expert E of weight arrays of E + 1 experts.
 """
 
 from __future__ import annotations
@@ -39,7 +46,7 @@ import numpy as np
 
 GROUP_SIZE = 32
 
-_STREAMS = ("logits", "x", "w13_q", "w13_z", "w13_s", "w2_q", "w2_z", "w2_s")
+_STREAMS = ("logits", "x", "w13_q", "w13_z", "w13_s", "w2_q", "w2_z", "w2_s", "gate_w")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -126,4 +133,22 @@ def make_inputs(shape: MoEShape, seed: int = 0) -> dict[str, np.ndarray]:
     """All inputs of one layer call: activations plus weights."""
     out = make_activations(shape, seed)
     out.update(make_weights(shape, seed))
+    return out
+
+
+def make_gate_weight(shape: MoEShape, seed: int = 0) -> np.ndarray:
+    """Router gate projection [E, H] fp16, N(0, 1/H)."""
+    shape.validate()
+    r = _rngs(seed)["gate_w"]
+    w = r.standard_normal((shape.E, shape.H), dtype=np.float32) * np.float32(1.0 / np.sqrt(shape.H))
+    return np.ascontiguousarray(w.astype(np.float16))
+
+
+def make_block_inputs(shape: MoEShape, seed: int = 0, shared: bool = True) -> dict[str, np.ndarray]:
+    """Inputs of the MoE block: x, the gate projection and the weights of the E
+    routed experts, followed by the shared expert's (index E) when ``shared``.
+    The drawn logits are kept too, for calls that take logits directly."""
+    out = make_activations(shape, seed)
+    out.update(make_weights(dataclasses.replace(shape, E=shape.E + int(shared)), seed))
+    out["gate_w"] = make_gate_weight(shape, seed)
     return out
