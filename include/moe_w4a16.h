@@ -15,6 +15,10 @@
  *   moe_w4a16_grouped_ffn  dequant-fused gate/up GEMM, SiLU(gate)*up, down GEMM
  *   moe_combine            router-weighted sum back to token order
  *
+ * Around it (the MoE block): moe_router_gate makes the logits from the
+ * activations, and a shared expert runs on every token beside the routed
+ * ones (moe_route_shared, moe_block_forward).
+ *
  * Conventions for every entry point
  *   - Pointers to tensors are DEVICE pointers unless stated otherwise; fp16
  *     tensors are passed as uint16_t bit patterns.  Every non-null tensor
@@ -98,6 +102,46 @@ int moe_abi_version(void);
  */
 int moe_route(const float* logits, int64_t T, int32_t E, int32_t top_k,
               int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
+ * moe_router_gate - the router's gate projection in front of moe_route:
+ * logits[t, e] = sum_h x[t, h] * gate_weight[e, h], fp16 inputs, products
+ * exact, sums in fp32.  "[Perf][SM70] Narrow Qwen3.8 AWQ active grouped
+ * decode", section "Capacity, startup, and remaining limit", names this
+ * projection among the costs beside the routed experts; the pages give no
+ * formula, so this is the plain linear map without bias, with an unquantised
+ * fp16 weight.  T <= 16: one GEMV launch bound by reading gate_weight; more
+ * tokens: a matrix-core GEMM.  The order of every sum is fixed.
+ *
+ *   x            in   fp16 [T, H]
+ *   gate_weight  in   fp16 [E, H]
+ *   logits       out  fp32 [T, E]
+ *
+ * Limits: 1 <= E <= 4096; H a multiple of 32, <= 16384; T * H < 2^31.
+ */
+int moe_router_gate(const uint16_t* x, int64_t T, int32_t H,
+                    const uint16_t* gate_weight, int32_t E, float* logits,
+                    void* stream);
+
+/*
+ * moe_route_shared - moe_route for a layer with a shared expert: row t of
+ * the outputs holds top_k + 1 entries, the top_k routed choices exactly as
+ * moe_route gives them, then the shared expert, id E, with weight 1.  The
+ * shared expert runs on every token with weight 1 beside the routed ones
+ * ("[Perf][SM70] Narrow Qwen3.8 AWQ active grouped decode", section
+ * "New-base bounded integration acceptance (r2)", names the shared overlap);
+ * with these rows the permutation, the FFN and the combine treat it as expert
+ * E of E + 1 experts, whose weights follow the routed experts' in the weight
+ * arrays.
+ *
+ *   logits        in   fp32  [T, E]
+ *   topk_ids      out  int32 [T, top_k + 1]
+ *   topk_weights  out  fp32  [T, top_k + 1]
+ *
+ * Limits: as moe_route with top_k + 1 <= 64 and E + 1 <= 4096.
+ */
+int moe_route_shared(const float* logits, int64_t T, int32_t E, int32_t top_k,
+                     int32_t* topk_ids, float* topk_weights, void* stream);
 
 /* Workspace bytes moe_permute needs for these sizes (0 when T <= 64). */
 size_t moe_permute_workspace_bytes(int64_t T, int32_t top_k, int32_t E);
@@ -270,6 +314,45 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T,
                       const int32_t* w2_qzeros, int32_t H, int32_t I,
                       int32_t group_size, uint16_t* out, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_block_forward needs for these sizes (0: invalid sizes). */
+size_t moe_block_workspace_bytes(int64_t T, int32_t top_k, int32_t E,
+                                 int32_t shared, int32_t H, int32_t I);
+
+/*
+ * moe_block_forward - the MoE block: moe_router_gate, then the routed layer,
+ * plus the shared expert when shared == 1.  With shared == 0 it is
+ * moe_router_gate followed by moe_layer_forward; with shared == 1 it is
+ * moe_router_gate, moe_route_shared, then moe_permute, moe_w4a16_grouped_ffn
+ * and moe_combine over E + 1 experts and top_k + 1 slots per token, so the
+ * shared expert's rows run in the same launches as the routed experts' rows
+ * and its output (weight 1) joins the fp32 sum before the one rounding to
+ * fp16.  out is what those calls produce, bit for bit.  Sections as
+ * moe_router_gate and moe_route_shared.
+ *
+ *   x            in   fp16 [T, H]
+ *   gate_weight  in   fp16 [E, H]
+ *   shared       0 or 1
+ *   w13_*, w2_*  in   as moe_w4a16_grouped_ffn, for E + shared experts
+ *                     (the shared expert is expert E)
+ *   group_size   must be 32
+ *   logits       out  fp32 [T, E]
+ *   out          out  fp16 [T, H]
+ *   workspace    scratch, device, >= moe_block_workspace_bytes(...) bytes;
+ *                contents on entry are ignored.  After the call it holds the
+ *                layout of moe_layer_forward's workspace for top_k + shared
+ *                slots per token and E + shared experts.
+ *
+ * Errors as the calls it stands for; nothing is enqueued on an error.
+ */
+int moe_block_forward(const uint16_t* x, int64_t T, const uint16_t* gate_weight,
+                      int32_t E, int32_t top_k, int32_t shared,
+                      const int32_t* w13_qweight, const uint16_t* w13_scales,
+                      const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                      const uint16_t* w2_scales, const int32_t* w2_qzeros,
+                      int32_t H, int32_t I, int32_t group_size, float* logits,
+                      uint16_t* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Scratch bytes of moe_layer_forward_noalloc (per device). */
 #define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = ops.load_library()
-    assert lib.moe_abi_version() == 100
+    assert lib.moe_abi_version() == 101
     for st in range(5):
         assert len(ops.status_string(st)) > 0
     assert ops.status_string(99) == "unknown status"
@@ -130,6 +130,58 @@ def test_combine_rejects_bad_arguments():
     assert lib.moe_combine(FAKE, FAKE, None, 8, 10, 2560, FAKE, None) == ops.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(FAKE, FAKE, FAKE, 8, 0, 2560, FAKE, None) == ops.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(None, None, None, 0, 10, 2560, None, None) == ops.MOE_OK
+
+
+def test_router_gate_rejects_bad_arguments():
+    lib = ops.load_library()
+    assert lib.moe_router_gate(FAKE, 8, 2570, FAKE, 512, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_gate(FAKE, 8, 2560, FAKE, 0, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_gate(FAKE, -1, 2560, FAKE, 512, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_gate(FAKE, 8, 2560, FAKE, 5000, FAKE, None) == ops.MOE_ERR_UNSUPPORTED
+    assert lib.moe_router_gate(FAKE, 8, 32768, FAKE, 512, FAKE, None) == ops.MOE_ERR_UNSUPPORTED
+    # x is addressed with 32-bit byte offsets: T * H < 2^31
+    assert lib.moe_router_gate(FAKE, (1 << 31) // 2560 + 1, 2560, FAKE, 512, FAKE,
+                               None) == ops.MOE_ERR_UNSUPPORTED
+    assert lib.moe_router_gate(None, 8, 2560, FAKE, 512, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_gate(FAKE, 8, 2560, FAKE + 2, 512, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_gate(FAKE, 8, 2560, FAKE, 512, None, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_gate(None, 0, 2560, None, 512, None, None) == ops.MOE_OK
+
+
+def test_route_shared_rejects_bad_arguments():
+    lib = ops.load_library()
+    # the shared expert takes one more slot and one more expert id
+    assert lib.moe_route_shared(FAKE, 4, 512, 64, FAKE, FAKE, None) == ops.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_shared(FAKE, 4, 512, 63, None, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_shared(FAKE, 4, 4096, 8, FAKE, FAKE, None) == ops.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_shared(FAKE, 4, 8, 9, FAKE, FAKE, None) == ops.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_shared(None, 0, 8, 2, None, None, None) == ops.MOE_OK
+
+
+def _block(lib, T=8, k=10, E=512, shared=1, H=2560, I=640, gs=32, ws_bytes=1 << 30,
+           gate=FAKE, logits=FAKE):
+    p = [FAKE] * 6
+    return lib.moe_block_forward(FAKE, T, gate, E, k, shared, *p, H, I, gs, logits, FAKE, FAKE,
+                                 ws_bytes, None)
+
+
+def test_block_rejects_bad_arguments():
+    lib = ops.load_library()
+    assert _block(lib, shared=2) == ops.MOE_ERR_INVALID_ARG
+    assert _block(lib, gs=64) == ops.MOE_ERR_UNSUPPORTED
+    assert _block(lib, H=2570) == ops.MOE_ERR_INVALID_ARG
+    assert _block(lib, ws_bytes=64) == ops.MOE_ERR_WORKSPACE
+    assert _block(lib, gate=None) == ops.MOE_ERR_INVALID_ARG
+    assert _block(lib, logits=FAKE + 4) == ops.MOE_ERR_INVALID_ARG
+    assert _block(lib, k=64) == ops.MOE_ERR_UNSUPPORTED      # top_k + 1 slots > 64
+    assert _block(lib, T=0) == ops.MOE_OK
+    need1 = ops.block_workspace_bytes(8, 10, 512, True, 2560, 640)
+    need0 = ops.block_workspace_bytes(8, 10, 512, False, 2560, 640)
+    assert need0 == ops.layer_workspace_bytes(8, 10, 512, 2560, 640)
+    assert need1 == ops.layer_workspace_bytes(8, 11, 513, 2560, 640) and need1 > need0
+    assert _block(lib, ws_bytes=need1 - 1) == ops.MOE_ERR_WORKSPACE
+    assert lib.moe_block_workspace_bytes(8, 10, 512, 2, 2560, 640) == 0
+    assert lib.moe_block_workspace_bytes(8, 64, 512, 1, 2560, 640) == 0
 
 
 def test_binding_refuses_to_run_without_library(tmp_path, monkeypatch):

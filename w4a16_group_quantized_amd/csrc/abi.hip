@@ -39,6 +39,14 @@ int check_prefill(int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
   return MOE_OK;
 }
 
+// The projection addresses x and Wg with 32-bit byte offsets.
+int check_router_gate(int64_t T, int32_t H, int32_t E) {
+  if (T < 0 || E < 1 || H <= 0 || H % kGroup) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts || H / kGroup > kMaxGroups) return MOE_ERR_UNSUPPORTED;
+  if (T * static_cast<int64_t>(H) * 2 >= (static_cast<int64_t>(1) << 32)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 int check_dims(int32_t H, int32_t I, int32_t group_size) {
   if (group_size != kGroup) return MOE_ERR_UNSUPPORTED;
   if (H <= 0 || I <= 0 || H % kGroup || I % kGroup) return MOE_ERR_INVALID_ARG;
@@ -115,15 +123,36 @@ const char* moe_status_string(int status) {
   }
 }
 
-int moe_abi_version(void) { return 100; }
+int moe_abi_version(void) { return 101; }
 
 int moe_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t* topk_ids,
               float* topk_weights, void* stream) {
   if (int st = check_routing(T, top_k, E)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(logits) || !ok_ptr(topk_ids) || !ok_ptr(topk_weights)) return MOE_ERR_INVALID_ARG;
-  launch_route(logits, static_cast<int>(T), E, top_k, topk_ids, topk_weights,
+  launch_route(logits, static_cast<int>(T), E, top_k, 0, topk_ids, topk_weights,
                static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+int moe_route_shared(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t* topk_ids,
+                     float* topk_weights, void* stream) {
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (int st = check_routing(T, top_k + 1, E + 1)) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(logits) || !ok_ptr(topk_ids) || !ok_ptr(topk_weights)) return MOE_ERR_INVALID_ARG;
+  launch_route(logits, static_cast<int>(T), E, top_k, 1, topk_ids, topk_weights,
+               static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
+int moe_router_gate(const uint16_t* x, int64_t T, int32_t H, const uint16_t* gate_weight,
+                    int32_t E, float* logits, void* stream) {
+  if (int st = check_router_gate(T, H, E)) return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(gate_weight) || !ok_ptr(logits)) return MOE_ERR_INVALID_ARG;
+  launch_router_gate(x, static_cast<int>(T), H, gate_weight, E, logits,
+                     static_cast<hipStream_t>(stream));
   return check_launch();
 }
 
@@ -164,7 +193,7 @@ int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t top_k,
   const size_t need = permute_workspace_bytes(T, E);
   if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
   if (need > 0 && !ok_ptr(workspace)) return MOE_ERR_INVALID_ARG;
-  launch_route_permute(logits, static_cast<int>(T), E, top_k, topk_ids, topk_weights,
+  launch_route_permute(logits, static_cast<int>(T), E, top_k, 0, topk_ids, topk_weights,
                        expert_offsets, sorted_slots, slot_rows, active_experts, num_active,
                        workspace, static_cast<hipStream_t>(stream));
   return check_launch();
@@ -338,31 +367,52 @@ size_t moe_layer_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H,
   return layer_ws(nullptr, T, top_k, E, H, I).total;
 }
 
-static int layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t E,
-                         int32_t top_k, const int32_t* w13_qweight, const uint16_t* w13_scales,
-                         const int32_t* w13_qzeros, const int32_t* w2_qweight,
-                         const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t H, int32_t I,
-                         int32_t group_size, uint16_t* out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+// Sizes and pointers of a layer call (the shared expert, when `shared` is 1,
+// adds one slot per token and one expert); MOE_OK or the error to return.
+static int layer_check(const float* logits, const uint16_t* x, int64_t T, int32_t E,
+                       int32_t top_k, int32_t shared, const int32_t* w13_qweight,
+                       const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                       const int32_t* w2_qweight, const uint16_t* w2_scales,
+                       const int32_t* w2_qzeros, int32_t H, int32_t I, int32_t group_size,
+                       const uint16_t* out, const void* workspace, size_t workspace_bytes) {
+  if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
   if (int st = check_routing(T, top_k, E)) return st;
+  if (int st = check_routing(T, top_k + shared, E + shared)) return st;
   if (int st = check_dims(H, I, group_size)) return st;
-  if (int st = check_prefill(T, top_k, E, H, I)) return st;
+  if (int st = check_prefill(T, top_k + shared, E + shared, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) ||
       !ok_ptr(w13_qzeros) || !ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) ||
       !ok_ptr(out) || !ok_ptr(workspace))
     return MOE_ERR_INVALID_ARG;
-  const LayerWs w = layer_ws(workspace, T, top_k, E, H, I);
-  if (workspace_bytes < w.total) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < layer_ws(nullptr, T, top_k + shared, E + shared, H, I).total)
+    return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// Enqueues a layer call that layer_check accepted.  With the shared expert
+// the routing gives every token one more slot, (expert E, weight 1), and the
+// permutation, the FFN and the combine run over E + 1 experts and top_k + 1
+// slots, so the shared expert's rows go through the same launches as the
+// routed experts' rows.
+static int layer_run(const float* logits, const uint16_t* x, int64_t T, int32_t E, int32_t top_k,
+                     int32_t shared, const int32_t* w13_qweight, const uint16_t* w13_scales,
+                     const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                     const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t H, int32_t I,
+                     int32_t group_size, uint16_t* out, void* workspace, void* stream) {
+  if (T == 0) return MOE_OK;
+  const int32_t kk = top_k + shared, EP = E + shared;
+  const LayerWs w = layer_ws(workspace, T, kk, EP, H, I);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (route_in_gate_up(T, E)) {
+  if (route_in_gate_up(T, EP)) {
     // decode: the gate/up kernel routes the tokens itself
-    const FfnWorkspace fws = ffn_workspace_carve(w.ffn, T, top_k, E, H, I);
+    const FfnWorkspace fws = ffn_workspace_carve(w.ffn, T, kk, EP, H, I);
     GateUpArgs a{};
     a.x = x;
     a.T = static_cast<int>(T);
-    a.top_k = top_k;
-    a.E = E;
+    a.top_k = kk;
+    a.E = EP;
+    a.shared = shared;
     a.H = H;
     a.I = I;
     a.qw = w13_qweight;
@@ -372,8 +422,8 @@ static int layer_forward(const float* logits, const uint16_t* x, int64_t T, int3
     launch_route_gate_up_decode(logits, a, r, fws, st);
     DownArgs d{};
     d.T = static_cast<int>(T);
-    d.top_k = top_k;
-    d.E = E;
+    d.top_k = kk;
+    d.E = EP;
     d.H = H;
     d.I = I;
     d.offsets = w.offsets;
@@ -385,17 +435,31 @@ static int layer_forward(const float* logits, const uint16_t* x, int64_t T, int3
     d.y = w.y;
     launch_down_decode(d, fws, st);
   } else {
-    launch_route_permute(logits, static_cast<int>(T), E, top_k, w.ids, w.weights, w.offsets,
-                         w.sorted, w.slot_rows, w.active, w.num_active, w.perm, st);
+    launch_route_permute(logits, static_cast<int>(T), E, top_k, shared, w.ids, w.weights,
+                         w.offsets, w.sorted, w.slot_rows, w.active, w.num_active, w.perm, st);
     if (int e = check_launch()) return e;
-    if (int e = moe_w4a16_grouped_ffn(x, T, top_k, w.offsets, w.sorted, w.active, w.num_active,
+    if (int e = moe_w4a16_grouped_ffn(x, T, kk, w.offsets, w.sorted, w.active, w.num_active,
                                       w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
-                                      w2_qzeros, E, H, I, group_size, w.y, w.ffn, w.ffn_bytes,
+                                      w2_qzeros, EP, H, I, group_size, w.y, w.ffn, w.ffn_bytes,
                                       stream))
       return e;
   }
-  launch_combine(w.y, w.weights, w.slot_rows, static_cast<int>(T), top_k, H, out, st);
+  launch_combine(w.y, w.weights, w.slot_rows, static_cast<int>(T), kk, H, out, st);
   return check_launch();
+}
+
+static int layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t E,
+                         int32_t top_k, int32_t shared, const int32_t* w13_qweight,
+                         const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                         const int32_t* w2_qweight, const uint16_t* w2_scales,
+                         const int32_t* w2_qzeros, int32_t H, int32_t I, int32_t group_size,
+                         uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int st = layer_check(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
+                           w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace,
+                           workspace_bytes))
+    return st;
+  return layer_run(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
+                   w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace, stream);
 }
 
 int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t E, int32_t top_k,
@@ -404,9 +468,40 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t
                       const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t H, int32_t I,
                       int32_t group_size, uint16_t* out, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  return layer_forward(logits, x, T, E, top_k, w13_qweight, w13_scales, w13_qzeros, w2_qweight,
-                       w2_scales, w2_qzeros, H, I, group_size, out, workspace, workspace_bytes,
-                       stream);
+  return layer_forward(logits, x, T, E, top_k, 0, w13_qweight, w13_scales, w13_qzeros,
+                       w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace,
+                       workspace_bytes, stream);
+}
+
+size_t moe_block_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t shared, int32_t H,
+                                 int32_t I) {
+  if (shared != 0 && shared != 1) return 0;
+  if (check_routing(T, top_k, E) != MOE_OK || check_routing(T, top_k + shared, E + shared) != MOE_OK ||
+      check_dims(H, I, kGroup) != MOE_OK)
+    return 0;
+  return layer_ws(nullptr, T, top_k + shared, E + shared, H, I).total;
+}
+
+int moe_block_forward(const uint16_t* x, int64_t T, const uint16_t* gate_weight, int32_t E,
+                      int32_t top_k, int32_t shared, const int32_t* w13_qweight,
+                      const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                      const int32_t* w2_qweight, const uint16_t* w2_scales,
+                      const int32_t* w2_qzeros, int32_t H, int32_t I, int32_t group_size,
+                      float* logits, uint16_t* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  // everything is checked before the projection is enqueued
+  if (int st = check_router_gate(T, H, E)) return st;
+  if (int st = layer_check(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
+                           w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace,
+                           workspace_bytes))
+    return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(gate_weight)) return MOE_ERR_INVALID_ARG;
+  launch_router_gate(x, static_cast<int>(T), H, gate_weight, E, logits,
+                     static_cast<hipStream_t>(stream));
+  if (int e = check_launch()) return e;
+  return layer_run(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
+                   w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace, stream);
 }
 
 }  // extern "C"
@@ -459,7 +554,7 @@ extern "C" int moe_layer_forward_noalloc(const float* logits, const uint16_t* x,
   int err = MOE_OK;
   void* ws = device_scratch(&err);
   if (ws == nullptr) return err;
-  return layer_forward(logits, x, T, E, top_k, w13_qweight, w13_scales, w13_qzeros, w2_qweight,
-                       w2_scales, w2_qzeros, H, I, group_size, out, ws, MOE_NOALLOC_SCRATCH_BYTES,
-                       stream);
+  return layer_forward(logits, x, T, E, top_k, 0, w13_qweight, w13_scales, w13_qzeros,
+                       w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, ws,
+                       MOE_NOALLOC_SCRATCH_BYTES, stream);
 }

@@ -29,7 +29,9 @@ DeviceInfo device_info();
 // Launchers (each enqueues on `stream`, returns nothing; the ABI layer checks
 // hipGetLastError afterwards).
 // ----------------------------------------------------------------------------
-void launch_route(const float* logits, int T, int E, int top_k, int* ids,
+// shared = 1: ids/weights rows have top_k + 1 entries, the last the shared
+// expert E with weight 1.
+void launch_route(const float* logits, int T, int E, int top_k, int shared, int* ids,
                   float* weights, hipStream_t stream);
 
 size_t permute_workspace_bytes(int64_t T, int E);
@@ -38,11 +40,17 @@ void launch_permute(const int* ids, int T, int top_k, int E, int* offsets,
                     int* num_active, void* workspace, hipStream_t stream);
 
 // Router and permutation in one call: one launch when route_permute_fused(T,
-// E) (small T), else the two launches above.
+// E + shared) (small T), else the two launches above.  E is the logits'
+// expert count; with shared = 1 the permutation covers E + 1 experts and
+// top_k + 1 slots per token.
 bool route_permute_fused(int64_t T, int E);
-void launch_route_permute(const float* logits, int T, int E, int top_k, int* ids,
+void launch_route_permute(const float* logits, int T, int E, int top_k, int shared, int* ids,
                           float* weights, int* offsets, int* sorted_slots, int* slot_rows,
                           int* active, int* num_active, void* workspace, hipStream_t stream);
+
+// Router gate projection logits[T, E] = x[T, H] . Wg[E, H]^T (router_gate.hip).
+void launch_router_gate(const uint16_t* x, int T, int H, const uint16_t* gate_weight, int E,
+                        float* logits, hipStream_t stream);
 
 struct FfnWorkspace {
   uint16_t* act_hi;  // [S, I] fp16, high part of SiLU(gate)*up
@@ -59,6 +67,7 @@ FfnWorkspace ffn_workspace_carve(void* base, int64_t T, int top_k, int E, int H,
 struct GateUpArgs {
   const uint16_t* x;
   int T, top_k, E, H, I;
+  int shared = 0;  // routing kernels only: top_k and E count a shared expert (index E - 1)
   const int* offsets;
   const int* sorted_slots;
   const int* active;

@@ -231,9 +231,13 @@ struct DecodeArgs {
   uint16_t* act_lo;
   float* y;                // stage 2 output
   // stage 1 that routes the tokens itself: logits in; the routing (as
-  // moe_route_permute returns it) written out by workgroup 0
+  // moe_route_permute returns it) written out by workgroup 0.  E and top_k
+  // count the shared expert when `shared` is 1: the logits then have E - 1
+  // columns, top_k - 1 choices are routed and slot top_k - 1 of every token
+  // is expert E - 1 with weight 1.
   const float* logits;
   int E;
+  int shared;
   int* r_ids;
   float* r_weights;
   int* r_offsets;
@@ -370,18 +374,21 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
     int* wtot = rnum + 1;
     for (int e = tid; e < E; e += kThreads) rmask[e] = 0ull;
     __syncthreads();
+    const int El = E - p.shared, kr = p.top_k - p.shared;  // logits columns, routed choices
     for (int t = wave; t < p.T; t += kWaves) {
       int id;
       float logit, top;
-      wave_topk<NPL>(p.logits + static_cast<size_t>(t) * E, E, p.top_k, id, logit, top);
-      const float w = wave_topk_weight(logit, top, p.top_k);
+      wave_topk<NPL>(p.logits + static_cast<size_t>(t) * El, El, kr, id, logit, top);
+      const float w = wave_topk_weight(logit, top, kr);
       if (lane < p.top_k) {
+        const bool sh = lane == kr;  // only when shared
         const int sl = t * p.top_k + lane;
-        rslot[sl] = id;
-        atomicOr(&rmask[id], 1ull << t);
+        const int e = sh ? El : id;
+        rslot[sl] = e;
+        atomicOr(&rmask[e], 1ull << t);
         if (blockIdx.x == 0) {
-          p.r_ids[sl] = id;
-          p.r_weights[sl] = w;
+          p.r_ids[sl] = e;
+          p.r_weights[sl] = sh ? 1.f : w;
         }
       }
     }
@@ -693,10 +700,11 @@ void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream,
   const size_t lds = launch_lds<GATE_UP>(geo, na) + rbytes;
   if constexpr (GATE_UP) {
     if (route) {
-      if (p.E <= 64) return launch_decode_npl<true, 1>(p, geo, na, lds, stream);
-      if (p.E <= 128) return launch_decode_npl<true, 2>(p, geo, na, lds, stream);
-      if (p.E <= 256) return launch_decode_npl<true, 4>(p, geo, na, lds, stream);
-      if (p.E <= 512) return launch_decode_npl<true, 8>(p, geo, na, lds, stream);
+      const int El = p.E - p.shared;  // logits per token
+      if (El <= 64) return launch_decode_npl<true, 1>(p, geo, na, lds, stream);
+      if (El <= 128) return launch_decode_npl<true, 2>(p, geo, na, lds, stream);
+      if (El <= 256) return launch_decode_npl<true, 4>(p, geo, na, lds, stream);
+      if (El <= 512) return launch_decode_npl<true, 8>(p, geo, na, lds, stream);
       return launch_decode_npl<true, 16>(p, geo, na, lds, stream);
     }
   }
@@ -754,6 +762,7 @@ void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const
   p.act_lo = ws.act_lo;
   p.logits = logits;
   p.E = a.E;
+  p.shared = a.shared;
   p.r_ids = r.ids;
   p.r_weights = r.weights;
   p.r_offsets = r.offsets;

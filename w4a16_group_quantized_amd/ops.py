@@ -40,6 +40,10 @@ EXPORTED = (
     "moe_layer_workspace_bytes",
     "moe_layer_forward",
     "moe_layer_forward_noalloc",
+    "moe_router_gate",
+    "moe_route_shared",
+    "moe_block_workspace_bytes",
+    "moe_block_forward",
 )
 
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -88,6 +92,13 @@ _SIGNATURES = {
     "moe_layer_forward_noalloc": (
         ctypes.c_int,
         [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P]),
+    "moe_router_gate": (ctypes.c_int, [_P, _I64, _I32, _P, _I32, _P, _P]),
+    "moe_route_shared": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
+    "moe_block_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32]),
+    "moe_block_forward": (
+        ctypes.c_int,
+        [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P,
+         _SZ, _P]),
 }
 
 
@@ -334,6 +345,83 @@ def moe_layer_forward_noalloc(logits: torch.Tensor, x: torch.Tensor, top_k: int,
         _ptr(logits), _ptr(x), T, E, top_k, _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w13_z"]),
         _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]), H, I, GROUP_SIZE, _ptr(out), _stream()))
     return out
+
+
+# --------------------------------------------------------------------------- #
+# the MoE block: router gate projection, shared expert
+# --------------------------------------------------------------------------- #
+def moe_router_gate(x: torch.Tensor, gate_weight: torch.Tensor, out: torch.Tensor | None = None):
+    """fp16 x [T, H], fp16 gate_weight [E, H] -> fp32 logits [T, E]."""
+    lib = load_library()
+    T, H = x.shape
+    E = gate_weight.shape[0]
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check("moe_router_gate", lib.moe_router_gate(_ptr(x), T, H, _ptr(gate_weight), E, _ptr(out),
+                                                  _stream()))
+    return out
+
+
+def moe_route_shared(logits: torch.Tensor, top_k: int):
+    """fp32 logits [T, E] -> (ids int32 [T, k+1], weights fp32 [T, k+1]); column k is the
+    shared expert E with weight 1."""
+    lib = load_library()
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, top_k + 1), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k + 1), dtype=torch.float32, device=dev)
+    _check("moe_route_shared", lib.moe_route_shared(_ptr(logits), T, E, top_k, _ptr(ids), _ptr(w),
+                                                    _stream()))
+    return ids, w
+
+
+def block_workspace_bytes(T: int, top_k: int, E: int, shared: bool, H: int, I: int) -> int:
+    return int(load_library().moe_block_workspace_bytes(T, top_k, E, int(shared), H, I))
+
+
+def moe_block_forward(x: torch.Tensor, gate_weight: torch.Tensor, top_k: int, w: dict,
+                      shared: bool = True, workspace: torch.Tensor | None = None,
+                      logits: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """The MoE block: projection, routed layer and (when ``shared``) the shared expert,
+    stored as expert E of the weight arrays.  Returns (out fp16 [T, H], logits fp32 [T, E])."""
+    lib = load_library()
+    T, H = x.shape
+    E = gate_weight.shape[0]
+    I = w["w2_q"].shape[2] * 8
+    dev = x.device
+    if workspace is None:
+        workspace = _workspace(block_workspace_bytes(T, top_k, E, shared, H, I), dev)
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float16, device=dev)
+    _check("moe_block_forward", lib.moe_block_forward(
+        _ptr(x), T, _ptr(gate_weight), E, top_k, int(shared), _ptr(w["w13_q"]), _ptr(w["w13_s"]),
+        _ptr(w["w13_z"]), _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]), H, I, GROUP_SIZE,
+        _ptr(logits), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out, logits
+
+
+class MoEBlock:
+    """Device-resident buffers for repeated block calls at one size (graph-capturable):
+    the projection, the routed experts and the shared expert in one entry point."""
+
+    def __init__(self, T: int, E: int, top_k: int, H: int, I: int, shared: bool = True,
+                 device="cuda"):
+        self.T, self.E, self.top_k, self.H, self.I, self.shared = T, E, top_k, H, I, shared
+        dev = torch.device(device)
+        self.ws = _workspace(block_workspace_bytes(T, top_k, E, shared, H, I), dev)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.float16, device=dev)
+
+    def __call__(self, x: torch.Tensor, gate_weight: torch.Tensor, w: dict) -> torch.Tensor:
+        moe_block_forward(x, gate_weight, self.top_k, w, self.shared, self.ws, self.logits,
+                          self.out)
+        return self.out
+
+    def views(self) -> dict:
+        k, E = self.top_k + int(self.shared), self.E + int(self.shared)
+        return layer_workspace_views(self.ws, self.T, k, E, self.H, self.I)
 
 
 # --------------------------------------------------------------------------- #
