@@ -2,10 +2,12 @@
 """Benchmark of the routed-expert W4A16 group-32 MoE layer on one MI355X.
 
 A step is one whole layer call (moe_layer_forward: router, permutation,
-grouped W4A16 FFN and combine; at decode sizes the gate/up kernel routes the
+grouped W4A16 FFN and combine; at decode sizes the first kernel routes the
 tokens itself) over one batch of seeded synthetic input with every input
 already resident in HBM.  The default workload is the 512-expert, top-10,
-hidden-2560, intermediate-640 layer at 8 decode tokens.
+hidden-2560, intermediate-640 layer at 8 decode tokens; the same run also
+measures the skewed 4096-token prefill (object `prefill`) and the MoE block
+around the decode layer, gate projection plus shared expert (object `block`).
 
 Measurement
   * The expert weights are cloned into --layers device copies and step s uses
@@ -16,14 +18,21 @@ Measurement
     issuing them: eagerly, replayed as HIP graphs of one step (one graph per
     weight copy), and replayed as one graph of `layers` consecutive steps
     (one per weight copy, as a model replays its layers), each bracketed by
-    device synchronisation (config.timing names which).
-    Before that the same K steps run eagerly as the four separate calls (moe_route_permute,
+    device synchronisation (config.timing names which).  Before that the same
+    K steps run eagerly as the separate calls the one call stands for (decode:
+    moe_route_gate_up, moe_w4a16_down, moe_combine; prefill: moe_route_permute,
     moe_w4a16_gate_up, moe_w4a16_down, moe_combine) with HIP events around
     each, for the per-stage breakdown, and the one-call step must reproduce
-    their output bit for bit.  The dominant kernel (gate/up, launched alone
-    back to back) gives the roofline.
+    their output bit for bit.
+  * roofline: the first FFN kernel of the timed step (decode: the routed
+    gate/up kernel of moe_route_gate_up; prefill: the gate/up call), launched
+    alone back to back on the routing of the batch, timed with HIP events on
+    its stream; achieved = its algorithmic bytes (or flops) per launch / its
+    average launch time.  layer_hbm_frac (top level) is the whole step's
+    algorithmic bytes / step time / 8 TB/s.
   * cpu_baseline: the CPU oracle (test infrastructure) timed on this host on
-    the same workload, best of a few repeats.
+    the same workload, best of a few repeats, with max |err| and relative RMS
+    of the GPU output against it on the same tokens.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -41,9 +50,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+METRIC = "MoE layer tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 matrix, AMD published
 DEFAULT_WORKLOAD = "decode_e512_k10_h2560_i640_t8"
+PREFILL_WORKLOAD = "prefill_zipf_e512_k10_h2560_i640_t4096"
+DECODE_MAX_T = 8               # token counts at or below this run the GEMV kernels
 
 
 def log(msg: str) -> None:
@@ -64,6 +76,12 @@ def parse_args(argv=None):
     p.add_argument("--no-graph", action="store_true", help="report the eager loop as value")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-repeats", type=int, default=3)
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the prefill object (measured by default with a decode workload)")
+    p.add_argument("--prefill-steps", type=int, default=24)
+    p.add_argument("--prefill-layers", type=int, default=4)
+    p.add_argument("--no-block", action="store_true",
+                   help="skip the block object (gate projection + shared expert)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB a few times (counter calibration)")
     return p.parse_args(argv)
@@ -95,32 +113,39 @@ def expert_bytes(H: int, I: int) -> tuple[int, int]:
 
 
 def layer_work(shape, num_active: int) -> dict:
-    w13, w2 = expert_bytes(shape.H, shape.I)
-    io = shape.T * shape.H * 2 + shape.T * shape.E * 4 + shape.T * shape.H * 2
+    """Bytes and flops per call.  gate_up: the active experts' w13, x, the act
+    pair written (and, when it routes, the logits read); down: w2, act read,
+    y_sorted written; layer: weights plus the layer's inputs and output."""
+    T, E, k, H, I = shape.T, shape.E, shape.top_k, shape.H, shape.I
+    S = T * k
+    w13, w2 = expert_bytes(H, I)
+    act = S * I * 2 * 2
     return {
         "w13_bytes_per_expert": w13,
         "w2_bytes_per_expert": w2,
-        "layer_bytes": num_active * (w13 + w2) + io,
-        "gate_up_bytes": num_active * w13 + shape.T * shape.H * 2,
-        "down_bytes": num_active * w2,
-        "flops": 6 * shape.T * shape.top_k * shape.H * shape.I,
-        "gate_up_flops": 4 * shape.T * shape.top_k * shape.H * shape.I,
+        "layer_bytes": num_active * (w13 + w2) + T * E * 4 + T * H * 2 + T * H * 2,
+        "gate_up_bytes": num_active * w13 + T * H * 2 + act,
+        "routed_gate_up_bytes": num_active * w13 + T * H * 2 + act + T * E * 4,
+        "down_bytes": num_active * w2 + act + S * H * 4,
+        "flops": 6 * S * H * I,
+        "gate_up_flops": 4 * S * H * I,
     }
 
 
+def routed_decode(shape) -> bool:
+    """The one-call layer routes inside its first kernel (moe_route_gate_up)."""
+    return shape.T <= DECODE_MAX_T and shape.E <= 1024
+
+
 # --------------------------------------------------------------------------- #
-# HBM traffic from rocprofv3 counters (committed summary, valid for one source)
+# HBM traffic and MFMA counters from committed rocprofv3 summaries
 # --------------------------------------------------------------------------- #
-DECODE_MAX_T = 8   # token counts at or below this run the GEMV kernels
-
-
-def kernel_sources(workload: str) -> list:
-    """Sources whose text fixes the FFN kernels a workload runs."""
-    from w4a16_group_quantized_amd.inputs import WORKLOADS
-
+def kernel_sources(T: int) -> list:
+    """Sources whose text fixes the kernels a workload's FFN runs."""
     csrc = "w4a16_group_quantized_amd/csrc/"
-    main = "ffn_decode.hip" if WORKLOADS[workload].T <= DECODE_MAX_T else "ffn_prefill.hip"
-    return [csrc + main, csrc + "common.h"]
+    if T <= DECODE_MAX_T:
+        return [csrc + "ffn_decode.hip", csrc + "common.h", csrc + "route.h", csrc + "permute.h"]
+    return [csrc + "ffn_prefill.hip", csrc + "common.h"]
 
 
 def source_sha256(rels: list) -> str:
@@ -133,60 +158,92 @@ def source_sha256(rels: list) -> str:
     return h.hexdigest()
 
 
-def counter_traffic(workload: str, kernel: str):
-    """Bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary.
-
-    profiles/counters_<workload>.md holds lines
-      traffic <kernel> fetch_kib=F write_kib=W fetch_scale=a write_scale=b source_sha256=S
-    where a and b scale each counter to bytes moved by a plain copy of known
-    size.  The figure is returned only while the kernel source still hashes
-    to S (otherwise the kernel changed since the counters were taken: None).
-    """
+def _summary_lines(workload: str, tag: str, name: str, T: int):
+    """key=value fields of line `<tag> <name> ...` in profiles/counters_<workload>.md,
+    or None when absent or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
     if not os.path.exists(path):
         return None
     for line in open(path):
         parts = line.split()
-        if len(parts) < 2 or parts[0] != "traffic" or parts[1] != kernel:
+        if len(parts) < 2 or parts[0] != tag or parts[1] != name:
             continue
         kv = dict(p.split("=", 1) for p in parts[2:])
-        if kv.get("source_sha256") != source_sha256(kernel_sources(workload)):
+        if kv.get("source_sha256") != source_sha256(kernel_sources(T)):
             return None
-        fetch = float(kv["fetch_kib"]) * float(kv["fetch_scale"]) * 1024
-        write = float(kv["write_kib"]) * float(kv["write_scale"]) * 1024
-        return fetch + write
+        return kv
     return None
+
+
+def counter_traffic(workload: str, kernel: str, T: int):
+    """HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what the counter reads for a plain copy of known size."""
+    kv = _summary_lines(workload, "traffic", kernel, T)
+    if kv is None:
+        return None
+    fetch = float(kv["fetch_kib"]) * float(kv["fetch_scale"]) * 1024
+    write = float(kv["write_kib"]) * float(kv["write_scale"]) * 1024
+    return fetch + write
+
+
+def mfma_util(workload: str, kernel: str, T: int):
+    kv = _summary_lines(workload, "mfma", kernel, T)
+    return None if kv is None else float(kv["util_pct"])
 
 
 # --------------------------------------------------------------------------- #
 # CPU baseline: the oracle on this host
 # --------------------------------------------------------------------------- #
-def cpu_baseline(host: dict, shape, repeats: int) -> dict:
-    import numpy as np
-
-    import oracle
-
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
 
         blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        threads = max(blas) if blas else 1
+        return max(blas) if blas else 1
     except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
-    sample_T = shape.T
-    sub = host
-    if shape.T > 64:  # bounded sample of the same workload: its first 64 tokens
-        sample_T = 64
-        sub = dict(host)
-        sub["logits"] = host["logits"][:64]
-        sub["x"] = host["x"][:64]
+        return 1
+
+
+ABS_TOL = 2e-2
+
+
+def error_figures(gpu_out, ref) -> dict:
+    """max |err| and relative RMS of the fp16 GPU output against the unrounded
+    oracle, and how many elements exceed 2e-2 only because no fp16 value lies
+    within 2e-2 of the exact one (|y| >= 64) while the GPU returned one of the
+    two fp16 values around it."""
+    import numpy as np
+
+    got = np.asarray(gpu_out, dtype=np.float16).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    r16 = ref.astype(np.float16)
+    below = r16.astype(np.float64) <= ref
+    lo = np.where(below, r16, np.nextafter(r16, np.float16(-np.inf))).astype(np.float64)
+    hi = np.where(below, np.nextafter(r16, np.float16(np.inf)), r16).astype(np.float64)
+    forced = ((err > ABS_TOL) & ((ref - lo) > ABS_TOL) & ((hi - ref) > ABS_TOL)
+              & ((got == lo) | (got == hi)))
+    return {"max_abs_err": float(err.max()),
+            "rel_rms": float(np.sqrt((err ** 2).sum() / (ref ** 2).sum())),
+            "n_over_2e-2_forced_by_fp16_spacing": int(forced.sum()),
+            "n_over_2e-2_other": int(((err > ABS_TOL) & ~forced).sum())}
+
+
+def cpu_baseline(host: dict, shape, repeats: int, gpu_out) -> dict:
+    import oracle
+
+    threads = _blas_threads()
+    sample_T = min(shape.T, 64)  # bounded sample of the same workload: its first tokens
+    sub = dict(host)
+    sub["logits"] = host["logits"][:sample_T]
+    sub["x"] = host["x"][:sample_T]
     best = float("inf")
+    ref = None
     for _ in range(max(1, repeats)):
         t0 = time.perf_counter()
-        oracle.layer(sub, shape.top_k)
+        ref = oracle.layer(sub, shape.top_k)
         best = min(best, time.perf_counter() - t0)
-    _ = np
-    return {
+    out = {
         "value": sample_T / best,
         "unit": "tokens/s",
         "cores": threads,
@@ -196,71 +253,134 @@ def cpu_baseline(host: dict, shape, repeats: int) -> dict:
                   f"{len(os.sched_getaffinity(0))} host cores visible",
         "seconds": best,
     }
+    out.update(error_figures(gpu_out[:sample_T], ref["out"]))
+    return out
 
 
 # --------------------------------------------------------------------------- #
-# GPU measurement
+# timing helpers (HIP events on the current stream)
 # --------------------------------------------------------------------------- #
-def main(argv=None) -> int:
-    args = parse_args(argv)
-    if args.copy_probe:
-        return copy_probe(args.copy_probe)
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build runs the MoE layer on a single MI355X "
-              "and has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
-        return 2
+def _events(n=2):
+    import torch
 
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def avg_ms(fn, steps: int, warm: int = 4) -> float:
+    """Average time of fn(i) over `steps` back-to-back calls."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        fn(i)
+    a, b = _events()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def graph_timings(step, copies: int, steps: int, warmup: int, check):
+    """(per-step graph ms, graph-of-`copies`-steps ms per step): step(c) captured once per
+    weight copy and replayed round-robin, then all `copies` steps captured as one graph.
+    check() must hold after replays."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    graphs = []
+    with torch.cuda.stream(cap):
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(c)
+            graphs.append(g)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    for rep in range(3):  # every replay must reproduce the eager result
+        graphs[rep % copies].replay()
+        torch.cuda.synchronize()
+        check(f"graph replay {rep}")
+    per_step = avg_ms(lambda i: graphs[i % copies].replay(), steps, warmup)
+    check("graph replays")
+
+    multi = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(multi, stream=cap):
+            for c in range(copies):
+                step(c)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    multi.replay()
+    torch.cuda.synchronize()
+    check("multi-step graph")
+    reps = max(1, steps // copies)
+    multi_ms = avg_ms(lambda i: multi.replay(), reps, max(1, warmup // copies)) / copies
+    return per_step, multi_ms
+
+
+def pick_timing(options: dict, steps: int, copies: int):
+    """The fastest way of issuing the same K steps; the multi-step graph counts
+    only when K is a whole number of its replays."""
+    opts = {k: v for k, v in options.items() if v is not None}
+    if f"hip-graph replay of {copies} layer steps" in opts and steps % copies:
+        opts.pop(f"hip-graph replay of {copies} layer steps")
+    timing = min(opts, key=opts.get)
+    return timing, opts[timing]
+
+
+def device_copies(w0: dict, n: int) -> list:
+    return [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(n - 1)]
+
+
+# --------------------------------------------------------------------------- #
+# the main workload
+# --------------------------------------------------------------------------- #
+def measure_layer(args, shape, workload: str, host: dict, dev, counters_apply: bool) -> dict:
+    """counters_apply: the committed byte counters were taken at this token count."""
     import numpy as np
     import torch
 
-    from w4a16_group_quantized_amd import inputs as synth
     from w4a16_group_quantized_amd import ops
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    shape = synth.WORKLOADS[args.workload]
-    if args.tokens is not None and args.tokens != shape.T:
-        shape = dataclasses.replace(shape, T=args.tokens)
-        shape.validate()
-    # byte counters were taken at the workload's own token count only
-    counters_apply = shape.T == synth.WORKLOADS[args.workload].T
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    ops.load_library()
-    log(f"workload {args.workload}: {shape} on {torch.cuda.get_device_name(dev)}")
-
-    host = synth.make_inputs(shape, args.seed)
     logits = torch.from_numpy(host["logits"]).to(dev)
     x = torch.from_numpy(host["x"]).to(dev)
-    w0 = ops.weights_to_device(host, dev)
-    copies = [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(args.layers - 1)]
-    per_copy = sum(v.numel() * v.element_size() for v in w0.values())
+    copies = device_copies(ops.weights_to_device(host, dev), args.layers)
+    per_copy = sum(v.numel() * v.element_size() for v in copies[0].values())
     log(f"{args.layers} weight copies x {per_copy / 2**30:.2f} GiB on device")
-
     layer = ops.MoELayer(shape.T, shape.E, shape.top_k, shape.H, shape.I, dev)
     stream = torch.cuda.current_stream()
+    routed = routed_decode(shape)
 
+    # the separate calls the one-call step stands for
     def step(i: int, ev=None):
         w = copies[i % args.layers]
-        if ev is not None:
-            ev[0].record(stream)
-        ops.moe_route_permute(logits, shape.top_k, layer.perm_ws, layer.ids, layer.weights,
-                              layer.perm)
-        if ev is not None:
-            ev[1].record(stream)
-        ops.moe_w4a16_gate_up(x, shape.top_k, layer.perm, w, layer.ffn_ws)
-        if ev is not None:
-            ev[2].record(stream)
-        ops.moe_w4a16_down(shape.T, shape.top_k, layer.perm, w, layer.y_sorted, layer.ffn_ws)
-        if ev is not None:
-            ev[3].record(stream)
-        ops.moe_combine(layer.y_sorted, layer.weights, layer.perm["slot_rows"], layer.out)
-        if ev is not None:
-            ev[4].record(stream)
 
-    # warm-up (eager), then the eager timed pass with per-call events
+        def mark(j):
+            if ev is not None:
+                ev[j].record(stream)
+
+        mark(0)
+        if routed:
+            ops.moe_route_gate_up(logits, x, shape.top_k, w, layer.ids, layer.weights, layer.perm,
+                                  layer.ffn_ws)
+            mark(1)
+            mark(2)
+        else:
+            ops.moe_route_permute(logits, shape.top_k, layer.perm_ws, layer.ids, layer.weights,
+                                  layer.perm)
+            mark(1)
+            ops.moe_w4a16_gate_up(x, shape.top_k, layer.perm, w, layer.ffn_ws)
+            mark(2)
+        ops.moe_w4a16_down(shape.T, shape.top_k, layer.perm, w, layer.y_sorted, layer.ffn_ws)
+        mark(3)
+        ops.moe_combine(layer.y_sorted, layer.weights, layer.perm["slot_rows"], layer.out)
+        mark(4)
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -268,67 +388,57 @@ def main(argv=None) -> int:
     num_active = int(layer.perm["num_active"].item())
     work = layer_work(shape, num_active)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    evs = [_events(5) for _ in range(args.steps)]
+    t0, t1 = _events()
     torch.cuda.synchronize()
-    t_start.record(stream)
+    t0.record(stream)
     for i in range(args.steps):
         step(i, evs[i])
-    t_end.record(stream)
+    t1.record(stream)
     torch.cuda.synchronize()
-    eager_ms = t_start.elapsed_time(t_end) / args.steps
-    seg = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])  # ms
-    seg_ms = seg.mean(axis=0)
-    log(f"eager: {eager_ms * 1e3:.1f} us/step; route+permute {seg_ms[0] * 1e3:.1f}, "
-        f"gate_up {seg_ms[1] * 1e3:.1f}, down {seg_ms[2] * 1e3:.1f}, combine {seg_ms[3] * 1e3:.1f} us")
+    eager_ms = t0.elapsed_time(t1) / args.steps
+    seg_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs]).mean(axis=0)
+    names = (["route+gate_up", None, "down", "combine"] if routed
+             else ["route+permute", "gate_up", "down", "combine"])
+    segments = {n: float(seg_ms[j] + (seg_ms[1] if routed and j == 0 else 0.0)) * 1e3
+                for j, n in enumerate(names) if n is not None}
+    log(f"eager separate calls: {eager_ms * 1e3:.1f} us/step; " +
+        ", ".join(f"{k} {v:.1f}" for k, v in segments.items()) + " us")
     assert torch.equal(layer.out, ref_out), "eager steps disagree"
 
-    # The dominant kernels alone: back-to-back launches on the routing of the
-    # batch (left in the layer's buffers), each on the next weight copy.
-    def kernel_avg_ms(launch) -> float:
-        for i in range(4):
-            launch(i)
-        k0 = torch.cuda.Event(enable_timing=True)
-        k1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        k0.record(stream)
-        for i in range(args.steps):
-            launch(i)
-        k1.record(stream)
-        torch.cuda.synchronize()
-        return k0.elapsed_time(k1) / args.steps
+    # the first FFN kernel alone, back to back on the batch's routing, each
+    # launch on the next weight copy
+    if routed:
+        gate_up_ms = avg_ms(lambda i: ops.moe_route_gate_up(
+            logits, x, shape.top_k, copies[i % args.layers], layer.ids, layer.weights, layer.perm,
+            layer.ffn_ws), args.steps)
+    else:
+        gate_up_ms = avg_ms(lambda i: ops.moe_w4a16_gate_up(
+            x, shape.top_k, layer.perm, copies[i % args.layers], layer.ffn_ws), args.steps)
+    down_ms = avg_ms(lambda i: ops.moe_w4a16_down(
+        shape.T, shape.top_k, layer.perm, copies[i % args.layers], layer.y_sorted, layer.ffn_ws),
+        args.steps)
+    log(f"back-to-back: {'routed ' if routed else ''}gate_up {gate_up_ms * 1e3:.1f} us, "
+        f"down {down_ms * 1e3:.1f} us")
 
-    gate_up_ms = kernel_avg_ms(lambda i: ops.moe_w4a16_gate_up(
-        x, shape.top_k, layer.perm, copies[i % args.layers], layer.ffn_ws))
-    down_ms = kernel_avg_ms(lambda i: ops.moe_w4a16_down(
-        shape.T, shape.top_k, layer.perm, copies[i % args.layers], layer.y_sorted, layer.ffn_ws))
-    log(f"back-to-back: gate_up {gate_up_ms * 1e3:.1f} us, down {down_ms * 1e3:.1f} us")
-
-    # The timed step: the whole layer as one moe_layer_forward call (which, at
-    # decode sizes, routes inside the gate/up kernel); it must give the four
-    # calls' output bit for bit.
+    # the timed step: one moe_layer_forward call, bit for bit the separate calls
     def layer_step(i: int):
         layer.forward(logits, x, copies[i % args.layers])
+
+    def check(what):
+        assert torch.equal(layer.fused_out, ref_out), f"{what} differs from the separate calls"
 
     layer.fused_out.zero_()
     layer_step(0)
     torch.cuda.synchronize()
-    assert torch.equal(layer.fused_out, ref_out), "moe_layer_forward differs from the four calls"
-    t_start.record(stream)
-    for i in range(args.steps):
-        layer_step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    fused_eager_ms = t_start.elapsed_time(t_end) / args.steps
+    check("moe_layer_forward")
+    fused_eager_ms = avg_ms(layer_step, args.steps, 0)
     log(f"eager moe_layer_forward: {fused_eager_ms * 1e3:.1f} us/step")
 
-    # Per-step spread of the same eager steps (events around each step), and a
-    # labelled hot-cache figure: every step on one weight copy, whose active
-    # experts then stay in the last-level cache (not a layer of a model).
+    # per-step spread of eager steps, and a labelled hot-cache figure (every
+    # step on one weight copy, whose active experts stay in the last-level cache)
     def per_step_us(copy_of) -> np.ndarray:
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+        ev = [_events() for _ in range(args.steps)]
         torch.cuda.synchronize()
         for i in range(args.steps):
             ev[i][0].record(stream)
@@ -343,94 +453,245 @@ def main(argv=None) -> int:
     log(f"eager steps p10/p50/p90 {step_pct['p10']:.1f} / {step_pct['p50']:.1f} / "
         f"{step_pct['p90']:.1f} us; hot-cache (one weight copy) p50 {np.median(hot):.1f} us")
 
-    # HIP graphs: one captured step per weight copy, replayed round-robin
-    graph_ms = None
-    graph_multi_ms = None
+    graph_ms = graph_multi_ms = None
     if not args.no_graph:
-        graphs = []
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            for c in range(args.layers):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cap):
-                    layer_step(c)
-                graphs.append(g)
-        stream.wait_stream(cap)
-        torch.cuda.synchronize()
-        for rep in range(3):  # every replay must reproduce the eager result
-            layer.fused_out.zero_()
-            graphs[rep % args.layers].replay()
-            torch.cuda.synchronize()
-            assert torch.equal(layer.fused_out, ref_out), "graph replay differs from eager"
-        for i in range(args.warmup):
-            graphs[i % args.layers].replay()
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        for i in range(args.steps):
-            graphs[i % args.layers].replay()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = t_start.elapsed_time(t_end) / args.steps
-        assert torch.equal(layer.fused_out, ref_out), "graph replay differs from eager"
-        log(f"graph: {graph_ms * 1e3:.1f} us/step")
+        graph_ms, graph_multi_ms = graph_timings(layer_step, args.layers, args.steps, args.warmup,
+                                                 check)
+        log(f"graph: {graph_ms * 1e3:.1f} us/step; graph of {args.layers} layer steps: "
+            f"{graph_multi_ms * 1e3:.1f} us/step")
+    timing, ms = pick_timing({"eager": fused_eager_ms, "hip-graph replay": graph_ms,
+                              f"hip-graph replay of {args.layers} layer steps": graph_multi_ms},
+                             args.steps, args.layers)
 
-        # A model step as one graph: `layers` consecutive layer steps (one per
-        # weight copy) captured together, as a decoder replays all its layers.
-        multi = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(multi, stream=cap):
-                for c in range(args.layers):
-                    layer_step(c)
-        stream.wait_stream(cap)
-        torch.cuda.synchronize()
-        layer.fused_out.zero_()
-        multi.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(layer.fused_out, ref_out), "multi-layer graph differs from eager"
-        reps = max(1, args.steps // args.layers)
-        for _ in range(max(1, args.warmup // args.layers)):
-            multi.replay()
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        for _ in range(reps):
-            multi.replay()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        graph_multi_ms = t_start.elapsed_time(t_end) / (reps * args.layers)
-        log(f"graph of {args.layers} layer steps: {graph_multi_ms * 1e3:.1f} us/step")
-
-    # the fastest of the ways of issuing the same K steps (the per-step
-    # HIP-graph replay pays a graph launch per step; the multi-layer graph
-    # counts only when K is a whole number of its replays)
-    options = {"eager": fused_eager_ms}
-    if graph_ms is not None:
-        options["hip-graph replay"] = graph_ms
-    if graph_multi_ms is not None and args.steps % args.layers == 0:
-        options[f"hip-graph replay of {args.layers} layer steps"] = graph_multi_ms
-    timing = min(options, key=options.get)
-    ms = options[timing]
-    tokens_per_s = shape.T / (ms * 1e-3)
+    # roofline of the first FFN kernel of the step
+    gu_bytes = work["routed_gate_up_bytes"] if routed else work["gate_up_bytes"]
     gate_up_s = gate_up_ms * 1e-3
-    intensity = work["gate_up_flops"] / work["gate_up_bytes"]
+    intensity = work["gate_up_flops"] / gu_bytes
     ridge = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if intensity < ridge:
-        roof = {"bound": "hbm", "achieved": work["gate_up_bytes"] / gate_up_s / 1e9,
+        roof = {"bound": "hbm", "achieved": gu_bytes / gate_up_s / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     else:
         roof = {"bound": "mfma", "achieved": work["gate_up_flops"] / gate_up_s / 1e12,
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = counter_traffic(args.workload, "gate_up") if counters_apply else None
+    ckey = "route_gate_up" if routed else "gate_up"
+    roof["traffic"] = counter_traffic(workload, ckey, shape.T) if counters_apply else None
     roof.update({
-        "kernel": "gate/up kernel of moe_w4a16_gate_up",
+        "kernel": ("routed gate/up kernel (moe_route_gate_up: router, permutation and gate/up in "
+                   "one launch, the first kernel of moe_layer_forward)" if routed
+                   else "gate/up call (moe_w4a16_gate_up: tile-list prep + gate/up GEMM)"),
         "avg_launch_us": gate_up_ms * 1e3,
-        "algorithmic_bytes_per_launch": work["gate_up_bytes"],
+        "algorithmic_bytes_per_launch": gu_bytes,
         "algorithmic_flops_per_launch": work["gate_up_flops"],
     })
+    layer_gbs = work["layer_bytes"] / (ms * 1e-3) / 1e9
+    return {
+        "ms": ms, "timing": timing, "num_active": num_active, "roofline": roof,
+        "gpu_out": ref_out.cpu().numpy(),
+        "layer": {
+            "eager_separate_calls_us_per_step": eager_ms * 1e3,
+            "eager_layer_forward_us_per_step": fused_eager_ms * 1e3,
+            "eager_step_us_percentiles": step_pct,
+            "hot_cache_us_per_step_p50": float(np.median(hot)),
+            "graph_us_per_step": graph_ms * 1e3 if graph_ms is not None else None,
+            "graph_multi_layer_us_per_step": (graph_multi_ms * 1e3 if graph_multi_ms is not None
+                                              else None),
+            "algorithmic_bytes": work["layer_bytes"],
+            "layer_GBps": layer_gbs,
+            "layer_hbm_frac": layer_gbs / HBM_PEAK_GBS,
+            "flops": work["flops"],
+            "TFLOPs": work["flops"] / (ms * 1e-3) / 1e12,
+            "mfma_frac": work["flops"] / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "segments_us": segments,
+            "down_kernel_us": down_ms * 1e3,
+            "down_algorithmic_bytes": work["down_bytes"],
+            "down_GBps": work["down_bytes"] / (down_ms * 1e-3) / 1e9,
+            "down_traffic": counter_traffic(workload, "down", shape.T) if counters_apply else None,
+        },
+    }
+
+
+# --------------------------------------------------------------------------- #
+# the skewed 4096-token prefill (MFMA half of the metric)
+# --------------------------------------------------------------------------- #
+def measure_prefill(args, workload: str, dev) -> dict:
+    import numpy as np
+    import torch
+
+    import oracle
+    from w4a16_group_quantized_amd import inputs as synth
+    from w4a16_group_quantized_amd import ops
+
+    shape = synth.WORKLOADS[workload]
+    host = synth.make_inputs(shape, args.seed)
+    logits = torch.from_numpy(host["logits"]).to(dev)
+    x = torch.from_numpy(host["x"]).to(dev)
+    n = args.prefill_layers
+    copies = device_copies(ops.weights_to_device(host, dev), n)
+    layer = ops.MoELayer(shape.T, shape.E, shape.top_k, shape.H, shape.I, dev)
+    steps = args.prefill_steps
+    log(f"prefill {workload}: {n} weight copies, {steps} steps")
+
+    layer(logits, x, copies[0])
+    torch.cuda.synchronize()
+    ref_out = layer.out.clone()
+
+    def layer_step(i: int):
+        layer.forward(logits, x, copies[i % n])
+
+    def check(what):
+        assert torch.equal(layer.fused_out, ref_out), f"prefill {what} differs from the separate calls"
+
+    layer_step(0)
+    torch.cuda.synchronize()
+    check("moe_layer_forward")
+    eager_ms = avg_ms(layer_step, steps, 2)
+    graph_ms, multi_ms = graph_timings(layer_step, n, steps, 2, check)
+    timing, ms = pick_timing({"eager": eager_ms, "hip-graph replay": graph_ms,
+                              f"hip-graph replay of {n} layer steps": multi_ms}, steps, n)
+    gate_up_ms = avg_ms(lambda i: ops.moe_w4a16_gate_up(x, shape.top_k, layer.perm, copies[i % n],
+                                                        layer.ffn_ws), steps, 2)
+    down_ms = avg_ms(lambda i: ops.moe_w4a16_down(shape.T, shape.top_k, layer.perm, copies[i % n],
+                                                  layer.y_sorted, layer.ffn_ws), steps, 2)
+    work = layer_work(shape, int(layer.perm["num_active"].item()))
+    tflops = work["flops"] / (ms * 1e-3) / 1e12
+    gu_tflops = work["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12
+    log(f"prefill: {ms * 1e3:.1f} us/step ({timing}), {tflops:.1f} TFLOP/s; gate_up call "
+        f"{gate_up_ms * 1e3:.1f} us, down {down_ms * 1e3:.1f} us")
+
+    # the output against the oracle on a few sampled tokens
+    tokens = np.linspace(0, shape.T - 1, 4).astype(np.int64)
+    ids, wts = oracle.route(host["logits"][tokens], shape.top_k)
+    sub_ids = np.zeros((shape.T, shape.top_k), np.int32)
+    sub_w = np.zeros((shape.T, shape.top_k))
+    sub_ids[tokens], sub_w[tokens] = ids, wts
+    ref = oracle.token_outputs(host, sub_ids, sub_w, tokens)
+    err = error_figures(ref_out.cpu().numpy()[tokens], ref)
+    util = mfma_util(workload, "gate_up", shape.T)
+    return {
+        "workload": workload,
+        "T": shape.T, "E": shape.E, "top_k": shape.top_k, "H": shape.H, "I": shape.I,
+        "us_per_step": ms * 1e3,
+        "timing": timing,
+        "tokens_per_s": shape.T / (ms * 1e-3),
+        "flops": work["flops"],
+        "TFLOPs": tflops,
+        "mfma_frac": tflops / MFMA_F16_PEAK_TFLOPS,
+        "layer_GBps": work["layer_bytes"] / (ms * 1e-3) / 1e9,
+        "gate_up_call_us": gate_up_ms * 1e3,
+        "gate_up_TFLOPs": gu_tflops,
+        "gate_up_mfma_frac": gu_tflops / MFMA_F16_PEAK_TFLOPS,
+        "down_kernel_us": down_ms * 1e3,
+        "gate_up_mfma_util_pct": util,
+        "mfma_util_source": (f"profiles/counters_{workload}.md (rocprofv3 MfmaUtil of the gate/up "
+                             "kernel; null when the kernel source changed since)"),
+        "oracle_check": dict(err, tokens=tokens.tolist()),
+        "weight_copies": n,
+    }
+
+
+# --------------------------------------------------------------------------- #
+# the MoE block around the decode layer: gate projection + shared expert
+# --------------------------------------------------------------------------- #
+def measure_block(args, shape, dev) -> dict:
+    import numpy as np
+    import torch
+
+    import oracle
+    from w4a16_group_quantized_amd import inputs as synth
+    from w4a16_group_quantized_amd import ops
+
+    host = synth.make_block_inputs(shape, args.seed, shared=True)
+    x = torch.from_numpy(host["x"]).to(dev)
+    n = args.layers
+    w0 = ops.weights_to_device(host, dev)
+    w0["gate_w"] = torch.from_numpy(host["gate_w"]).to(dev)
+    copies = device_copies(w0, n)
+    blk = ops.MoEBlock(shape.T, shape.E, shape.top_k, shape.H, shape.I, True, dev)
+
+    def step(i: int):
+        w = copies[i % n]
+        blk(x, w["gate_w"], w)
+
+    step(0)
+    torch.cuda.synchronize()
+    ref_out = blk.out.clone()
+
+    def check(what):
+        assert torch.equal(blk.out, ref_out), f"block {what} differs from eager"
+
+    eager_ms = avg_ms(step, args.steps, 4)
+    check("eager")
+    graph_ms = multi_ms = None
+    if not args.no_graph:
+        graph_ms, multi_ms = graph_timings(step, n, args.steps, args.warmup, check)
+    timing, ms = pick_timing({"eager": eager_ms, "hip-graph replay": graph_ms,
+                              f"hip-graph replay of {n} layer steps": multi_ms}, args.steps, n)
+    proj_ms = avg_ms(lambda i: ops.moe_router_gate(x, copies[i % n]["gate_w"], blk.logits),
+                     args.steps)
+    num_active = int(blk.views()["num_active"].item())  # the shared expert included
+    w13, w2 = expert_bytes(shape.H, shape.I)
+    proj_bytes = shape.E * shape.H * 2 + shape.T * shape.H * 2 + shape.T * shape.E * 4
+    block_bytes = num_active * (w13 + w2) + proj_bytes + shape.T * shape.H * 2
+    gbs = block_bytes / (ms * 1e-3) / 1e9
+    ref = oracle.block(host, shape.top_k, shared=True)
+    err = error_figures(ref_out.cpu().numpy(), ref["out"])
+    log(f"block (projection + routed + shared): {ms * 1e3:.1f} us/step ({timing}), "
+        f"{gbs:.0f} GB/s; projection {proj_ms * 1e3:.1f} us")
+    return {
+        "what": "moe_block_forward: gate projection, routed experts and the shared expert "
+                "(expert E, in the same launches)",
+        "T": shape.T, "E": shape.E, "top_k": shape.top_k, "H": shape.H, "I": shape.I,
+        "us_per_step": ms * 1e3,
+        "timing": timing,
+        "tokens_per_s": shape.T / (ms * 1e-3),
+        "active_experts_with_shared": num_active,
+        "algorithmic_bytes": block_bytes,
+        "GBps": gbs,
+        "hbm_frac": gbs / HBM_PEAK_GBS,
+        "projection_kernel_us": proj_ms * 1e3,
+        "projection_bytes": proj_bytes,
+        "projection_hbm_frac": proj_bytes / (proj_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "oracle_check": err,
+    }
+
+
+# --------------------------------------------------------------------------- #
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the MoE layer on a single MI355X "
+              "and has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from w4a16_group_quantized_amd import inputs as synth
+    from w4a16_group_quantized_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    shape = synth.WORKLOADS[args.workload]
+    if args.tokens is not None and args.tokens != shape.T:
+        shape = dataclasses.replace(shape, T=args.tokens)
+        shape.validate()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.load_library()
+    log(f"workload {args.workload}: {shape} on {torch.cuda.get_device_name(dev)}")
+
+    host = synth.make_inputs(shape, args.seed)
+    m = measure_layer(args, shape, args.workload, host, dev,
+                      shape.T == synth.WORKLOADS[args.workload].T)
+    ms = m["ms"]
     result = {
-        "metric": "MoE layer tokens/s (decode: HBM GB/s of the gate/up kernel in roofline)",
-        "value": tokens_per_s,
+        "metric": METRIC,
+        "value": shape.T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -444,34 +705,26 @@ def main(argv=None) -> int:
         "config": {
             "workload": args.workload,
             "E": shape.E, "top_k": shape.top_k, "H": shape.H, "I": shape.I, "T": shape.T,
-            "group_size": 32, "weight_copies": args.layers, "active_experts": num_active,
-            "timing": timing,
+            "group_size": 32, "weight_copies": args.layers, "active_experts": m["num_active"],
+            "timing": m["timing"],
         },
-        "roofline": roof,
-        "layer": {
-            "eager_us_per_step": eager_ms * 1e3,
-            "eager_layer_forward_us_per_step": fused_eager_ms * 1e3,
-            "eager_step_us_percentiles": step_pct,
-            "hot_cache_us_per_step_p50": float(np.median(hot)),
-            "graph_us_per_step": graph_ms * 1e3 if graph_ms is not None else None,
-            "graph_multi_layer_us_per_step": (graph_multi_ms * 1e3 if graph_multi_ms is not None
-                                              else None),
-            "algorithmic_bytes": work["layer_bytes"],
-            "layer_GBps": work["layer_bytes"] / (ms * 1e-3) / 1e9,
-            "layer_hbm_frac": work["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "flops": work["flops"],
-            "TFLOPs": work["flops"] / (ms * 1e-3) / 1e12,
-            "mfma_frac": work["flops"] / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
-            "segments_us": {"route+permute": seg_ms[0] * 1e3, "gate_up": seg_ms[1] * 1e3,
-                            "down": seg_ms[2] * 1e3, "combine": seg_ms[3] * 1e3},
-            "down_kernel_us": down_ms * 1e3,
-            "down_GBps": work["down_bytes"] / (down_ms * 1e-3) / 1e9,
-            "down_traffic": counter_traffic(args.workload, "down") if counters_apply else None,
-        },
+        "layer_GBps": m["layer"]["layer_GBps"],
+        "layer_hbm_frac": m["layer"]["layer_hbm_frac"],
+        "roofline": m["roofline"],
+        "layer": m["layer"],
     }
+    gpu_out = m.pop("gpu_out")
+    decode = shape.T <= DECODE_MAX_T
+    torch.cuda.empty_cache()
+    if decode and not args.no_block:
+        result["block"] = measure_block(args, shape, dev)
+        torch.cuda.empty_cache()
+    if decode and not args.no_prefill:
+        result["prefill"] = measure_prefill(args, PREFILL_WORKLOAD, dev)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(host, shape, args.cpu_repeats)
+        result["cpu_baseline"] = cpu_baseline(host, shape, args.cpu_repeats, gpu_out)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

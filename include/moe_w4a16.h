@@ -264,6 +264,36 @@ int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
                    size_t workspace_bytes, void* stream);
 
 /*
+ * moe_route_gate_up - the first launch of moe_layer_forward at decode sizes:
+ * the router, the permutation and the gate/up half of the FFN as one kernel
+ * (every workgroup routes the tokens itself, so none waits for another;
+ * workgroup 0 writes the routing out).  Its outputs equal those of
+ * moe_route_permute followed by moe_w4a16_gate_up, bit for bit, and feed
+ * moe_w4a16_down and moe_combine.  "[Perf][SM70] Narrow Qwen3.8 AWQ active
+ * grouped decode", section "Capacity, startup, and remaining limit", names
+ * each format's MoE preparation among the remaining decode costs; this takes
+ * the preparation's launch out of the step.
+ *
+ *   logits, x        in   as moe_layer_forward
+ *   w13_*            in   as moe_w4a16_grouped_ffn
+ *   topk_ids ... num_active   out  as moe_route_permute
+ *   workspace        FFN workspace (moe_ffn_workspace_bytes); holds act for
+ *                    moe_w4a16_down afterwards
+ *
+ * MOE_ERR_UNSUPPORTED unless T <= 8 and E <= 1024; other errors as the calls
+ * it stands for.
+ */
+int moe_route_gate_up(const float* logits, const uint16_t* x, int64_t T,
+                      int32_t E, int32_t top_k, const int32_t* w13_qweight,
+                      const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                      int32_t H, int32_t I, int32_t group_size,
+                      int32_t* topk_ids, float* topk_weights,
+                      int32_t* expert_offsets, int32_t* sorted_slots,
+                      int32_t* slot_rows, int32_t* active_experts,
+                      int32_t* num_active, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
  * moe_combine - router-weighted combine back to token order.
  *
  *   out[t, h] = fp16_rne( sum_{j = 0..top_k-1} topk_weights[t, j] *

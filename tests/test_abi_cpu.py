@@ -124,6 +124,22 @@ def test_gate_up_and_down_reject_bad_arguments():
                               None) == ops.MOE_ERR_WORKSPACE
 
 
+def test_route_gate_up_rejects_bad_arguments():
+    lib = ops.load_library()
+    p = [FAKE] * 8
+
+    def call(T=8, E=512, k=10, H=2560, I=640, gs=32, ws_bytes=1 << 30, logits=FAKE):
+        return lib.moe_route_gate_up(logits, FAKE, T, E, k, FAKE, FAKE, FAKE, H, I, gs, *p[:7],
+                                     FAKE, ws_bytes, None)
+
+    assert call(T=9) == ops.MOE_ERR_UNSUPPORTED        # decode sizes only
+    assert call(E=1025) == ops.MOE_ERR_UNSUPPORTED
+    assert call(gs=64) == ops.MOE_ERR_UNSUPPORTED
+    assert call(ws_bytes=64) == ops.MOE_ERR_WORKSPACE
+    assert call(logits=None) == ops.MOE_ERR_INVALID_ARG
+    assert call(T=0, logits=None) == ops.MOE_OK
+
+
 def test_combine_rejects_bad_arguments():
     lib = ops.load_library()
     assert lib.moe_combine(FAKE, FAKE, FAKE, 8, 10, 2561, FAKE, None) == ops.MOE_ERR_INVALID_ARG

@@ -26,10 +26,44 @@ def test_layer_work_of_the_decode_workload():
     shape = synth.WORKLOADS["decode_e512_k10_h2560_i640_t8"]
     work = bench.layer_work(shape, 73)
     io = 8 * 2560 * 2 + 8 * 512 * 4 + 8 * 2560 * 2
+    act = 80 * 640 * 2 * 2  # act as an fp16 hi/lo pair per sorted row
     assert work["layer_bytes"] == 73 * 2_841_600 + io
-    assert work["gate_up_bytes"] == 73 * 1_894_400 + 8 * 2560 * 2
+    assert work["gate_up_bytes"] == 73 * 1_894_400 + 8 * 2560 * 2 + act
+    assert work["routed_gate_up_bytes"] == work["gate_up_bytes"] + 8 * 512 * 4
+    assert work["down_bytes"] == 73 * 947_200 + act + 80 * 2560 * 4
     assert work["flops"] == 6 * 8 * 10 * 2560 * 640
     assert work["gate_up_flops"] == 4 * 8 * 10 * 2560 * 640
+
+
+def test_routed_decode_boundary():
+    """The one-call layer routes inside its first kernel at T <= 8 and E <= 1024."""
+    base = synth.WORKLOADS["decode_e512_k10_h2560_i640_t8"]
+    assert bench.routed_decode(base)
+    assert not bench.routed_decode(synth.MoEShape(E=512, top_k=10, H=2560, I=640, T=9))
+    assert not bench.routed_decode(synth.MoEShape(E=1025, top_k=10, H=2560, I=640, T=8))
+    assert bench.routed_decode(synth.MoEShape(E=1024, top_k=10, H=2560, I=640, T=1))
+
+
+def test_counter_lines_hold_only_for_their_sources(tmp_path, monkeypatch):
+    """A traffic or MfmaUtil line is used only while the kernel sources hash as recorded."""
+    import shutil
+
+    for rel in bench.kernel_sources(8):
+        dst = tmp_path / rel
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(ROOT, rel), dst)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    sha = bench.source_sha256(bench.kernel_sources(8))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "counters_w.md").write_text(
+        "text\n"
+        f"traffic down fetch_kib=100 write_kib=10 fetch_scale=2 write_scale=1 source_sha256={sha}\n"
+        f"mfma gate_up util_pct=31.5 source_sha256={sha}\n")
+    assert bench.counter_traffic("w", "down", 8) == (100 * 2 + 10) * 1024
+    assert bench.mfma_util("w", "gate_up", 8) == 31.5
+    assert bench.counter_traffic("w", "gate_up", 8) is None
+    (tmp_path / bench.kernel_sources(8)[0]).write_text("// changed\n")
+    assert bench.counter_traffic("w", "down", 8) is None
 
 
 def test_more_than_one_gpu_is_refused():

@@ -353,6 +353,35 @@ def test_layer_forward_against_oracle(dev):
     assert_fp16_close(out.cpu().numpy(), sub, f"{shape} moe_layer_forward")
 
 
+@pytest.mark.parametrize("E,k,H,I,T", [
+    (8, 2, 256, 128, 4), (512, 10, 2560, 640, 8), (512, 10, 2560, 160, 1), (1024, 8, 512, 256, 8),
+])
+def test_route_gate_up_steps_match_layer_forward(dev, E, k, H, I, T):
+    """moe_route_gate_up, moe_w4a16_down and moe_combine give moe_layer_forward's
+    output bit for bit, and the routing of moe_route_permute."""
+    from w4a16_group_quantized_amd import ops
+
+    shape = synth.MoEShape(E=E, top_k=k, H=H, I=I, T=T)
+    host = synth.make_inputs(shape, 12)
+    w = ops.weights_to_device(host, dev)
+    logits = torch.from_numpy(host["logits"]).to(dev)
+    x = torch.from_numpy(host["x"]).to(dev)
+    layer = ops.MoELayer(T, E, k, H, I, dev)
+    _poison(layer)
+    ops.moe_route_gate_up(logits, x, k, w, layer.ids, layer.weights, layer.perm, layer.ffn_ws)
+    ops.moe_w4a16_down(T, k, layer.perm, w, layer.y_sorted, layer.ffn_ws)
+    out = ops.moe_combine(layer.y_sorted, layer.weights, layer.perm["slot_rows"], layer.out)
+    fused = layer.forward(logits, x, w)
+    ids, wts, perm = ops.moe_route_permute(logits, k)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), fused.view(torch.int16))
+    assert torch.equal(ids, layer.ids) and torch.equal(wts.view(torch.int32), layer.weights.view(torch.int32))
+    for key, v in perm.items():
+        assert torch.equal(v, layer.perm[key]), key
+    ref = oracle.layer(host, k)
+    assert_fp16_close(out.cpu().numpy(), ref["out"], f"{shape}")
+
+
 def test_combine_alone(dev):
     from w4a16_group_quantized_amd import ops
 

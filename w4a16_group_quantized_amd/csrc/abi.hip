@@ -244,6 +244,40 @@ int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t
   return check_launch();
 }
 
+int moe_route_gate_up(const float* logits, const uint16_t* x, int64_t T, int32_t E, int32_t top_k,
+                      const int32_t* w13_qweight, const uint16_t* w13_scales,
+                      const int32_t* w13_qzeros, int32_t H, int32_t I, int32_t group_size,
+                      int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                      int32_t* sorted_slots, int32_t* slot_rows, int32_t* active_experts,
+                      int32_t* num_active, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (int st = check_dims(H, I, group_size)) return st;
+  if (!route_in_gate_up(T, E)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) ||
+      !ok_ptr(w13_qzeros) || !ok_ptr(topk_ids) || !ok_ptr(topk_weights) ||
+      !ok_ptr(expert_offsets) || !ok_ptr(sorted_slots) || !ok_ptr(slot_rows) ||
+      !ok_ptr(active_experts) || !ok_ptr(num_active) || !ok_ptr(workspace))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < ffn_workspace_bytes(T, top_k, E, H, I)) return MOE_ERR_WORKSPACE;
+  const FfnWorkspace ws = ffn_workspace_carve(workspace, T, top_k, E, H, I);
+  GateUpArgs a{};
+  a.x = x;
+  a.T = static_cast<int>(T);
+  a.top_k = top_k;
+  a.E = E;
+  a.H = H;
+  a.I = I;
+  a.qw = w13_qweight;
+  a.sc = w13_scales;
+  a.qz = w13_qzeros;
+  const RouteOut r{topk_ids, topk_weights, expert_offsets, sorted_slots, slot_rows,
+                   active_experts, num_active};
+  launch_route_gate_up_decode(logits, a, r, ws, static_cast<hipStream_t>(stream));
+  return check_launch();
+}
+
 int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
                    const int32_t* active_experts, const int32_t* num_active,
                    const int32_t* w2_qweight, const uint16_t* w2_scales, const int32_t* w2_qzeros,

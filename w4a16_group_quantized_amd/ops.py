@@ -36,6 +36,7 @@ EXPORTED = (
     "moe_w4a16_grouped_ffn",
     "moe_w4a16_gate_up",
     "moe_w4a16_down",
+    "moe_route_gate_up",
     "moe_combine",
     "moe_layer_workspace_bytes",
     "moe_layer_forward",
@@ -85,6 +86,10 @@ _SIGNATURES = {
         [_I64, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P],
     ),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_route_gate_up": (
+        ctypes.c_int,
+        [_P, _P, _I64, _I32, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+         _SZ, _P]),
     "moe_layer_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
     "moe_layer_forward": (
         ctypes.c_int,
@@ -272,6 +277,22 @@ def moe_w4a16_down(T: int, top_k: int, perm: dict, w: dict, y_sorted: torch.Tens
         T, top_k, _ptr(perm["expert_offsets"]), _ptr(perm["active_experts"]),
         _ptr(perm["num_active"]), _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]),
         E, H, I, GROUP_SIZE, _ptr(y_sorted), _ptr(workspace), workspace.numel(), _stream()))
+
+
+def moe_route_gate_up(logits: torch.Tensor, x: torch.Tensor, top_k: int, w: dict,
+                      ids: torch.Tensor, weights: torch.Tensor, perm: dict,
+                      workspace: torch.Tensor) -> None:
+    """Decode sizes (T <= 8): router, permutation and gate/up in one launch; the routing
+    goes to ids, weights and perm (as moe_route_permute), act to the FFN workspace."""
+    lib = load_library()
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w["w13_q"].shape[1] // 2
+    _check("moe_route_gate_up", lib.moe_route_gate_up(
+        _ptr(logits), _ptr(x), T, E, top_k, _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w13_z"]),
+        H, I, GROUP_SIZE, _ptr(ids), _ptr(weights), _ptr(perm["expert_offsets"]),
+        _ptr(perm["sorted_slots"]), _ptr(perm["slot_rows"]), _ptr(perm["active_experts"]),
+        _ptr(perm["num_active"]), _ptr(workspace), workspace.numel(), _stream()))
 
 
 def moe_combine(y_sorted: torch.Tensor, topk_weights: torch.Tensor, slot_rows: torch.Tensor,
