@@ -447,6 +447,7 @@ static int layer_run(const float* logits, const uint16_t* x, int64_t T, int32_t 
     a.top_k = kk;
     a.E = EP;
     a.shared = shared;
+    a.rows_hint = shared ? static_cast<int>(T) : 0;
     a.H = H;
     a.I = I;
     a.qw = w13_qweight;
@@ -458,6 +459,7 @@ static int layer_run(const float* logits, const uint16_t* x, int64_t T, int32_t 
     d.T = static_cast<int>(T);
     d.top_k = kk;
     d.E = EP;
+    d.rows_hint = a.rows_hint;
     d.H = H;
     d.I = I;
     d.offsets = w.offsets;

@@ -68,6 +68,7 @@ struct GateUpArgs {
   const uint16_t* x;
   int T, top_k, E, H, I;
   int shared = 0;  // routing kernels only: top_k and E count a shared expert (index E - 1)
+  int rows_hint = 0;  // decode: an expert may hold this many rows (a shared expert holds T)
   const int* offsets;
   const int* sorted_slots;
   const int* active;
@@ -78,6 +79,7 @@ struct GateUpArgs {
 };
 struct DownArgs {
   int T, top_k, E, H, I;
+  int rows_hint = 0;  // as in GateUpArgs
   const int* offsets;
   const int* active;
   const int* num_active;

@@ -41,7 +41,8 @@
 //
 // Precision of the down product.  act is stored as act_hi = fp16(act) and
 // act_lo = fp16(act - act_hi) and both halves are multiplied, which carries
-// act at about 22 bits instead of fp16's 11.
+// act at about 22 bits instead of fp16's 11: each half's group dot has its
+// bias removed on its own, and the two are added before the group's scale.
 #include <math.h>
 
 #include "common.h"
@@ -182,8 +183,20 @@ __device__ __forceinline__ float cluster_sum(float v, int C) {
 // ----------------------------------------------------------------- units ---
 // Work is cut into units (active-expert slot a, block b), numbered a * nb + b.
 // Workgroup w of nwg owns the units [U w / nwg, U (w + 1) / nwg), U =
-// num_active * nb, and works through them in windows of at most kXE experts
-// and wmax units.  For a window it stages in LDS the A rows of its experts
+// num_active * nb, when the experts' row counts are alike (routed experts at
+// decode sizes hold one or two rows).  When an expert may hold many rows (a
+// shared expert holds every token) units are shared out by cost instead: a
+// unit of an expert with r rows costs
+// passes(r) * kUnitBase + r (streaming its weights once per pass of na rows,
+// plus the arithmetic of each row), so an expert with many rows (a shared
+// expert runs on every token) spreads over more workgroups.  With P the
+// exclusive prefix of the per-unit costs over the active experts and
+// C = nb * P[num_active], unit (a, b) starts at cost nb * P[a] + b * cost(a),
+// and workgroup w of nwg owns the units that start in [C w / nwg,
+// C (w + 1) / nwg): a contiguous run of units, every unit owned exactly once.
+// The gate/up kernel computes P (one block scan) and workgroup 0 writes it to
+// the FFN workspace, where the down kernel reads it.  A workgroup works
+// through its units in windows of at most kXE experts and wmax units.  For a window it stages in LDS the A rows of its experts
 // (na rows per expert per pass; more passes when an expert has more rows),
 // then its 16 waves take units from an LDS counter until the window is done
 // (the first unit of wave i is unit w0 + i, primed before staging), each
@@ -197,8 +210,29 @@ struct Geom {
   int nb;    // blocks per expert
   int nwg;   // workgroups (one per compute unit)
   int wmax;  // units per window (bounded by LDS)
-  int u32;   // nonzero when E * nb * nwg < 2^32: the shares in 32-bit arithmetic
+  int ucap;  // ints of the LDS unit-cost table: prefix [slots + 1], then scan totals
+  int weighted;  // units shared out by cost (an expert holds many rows); else evenly
 };
+
+constexpr int kUnitBase = 4;  // cost of streaming a unit's weights once, in rows of arithmetic
+
+__device__ __forceinline__ int unit_cost(int rows, int na) {
+  return ((rows + na - 1) / na) * kUnitBase + rows;
+}
+
+// First unit whose start cost is >= c (num_active * nb when none), for the
+// per-unit cost prefix P[0..n] in LDS.
+__device__ __forceinline__ int first_unit(const int* P, int n, int nb, int64_t c) {
+  int lo = 0, hi = n;  // the largest a with nb * P[a] <= c (P[0] = 0 <= c)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (static_cast<int64_t>(nb) * P[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  if (lo == n) return n * nb;
+  const int64_t cost = P[lo + 1] - P[lo];
+  const int64_t b = (c - static_cast<int64_t>(nb) * P[lo] + cost - 1) / cost;
+  return b >= nb ? (lo + 1) * nb : lo * nb + static_cast<int>(b);
+}
 
 constexpr int kXE = 2;  // experts per window
 
@@ -230,6 +264,8 @@ struct DecodeArgs {
   uint16_t* act_hi;        // stage 1 outputs
   uint16_t* act_lo;
   float* y;                // stage 2 output
+  int* cost_out;           // stage 1: per-unit cost prefix [num_active + 1], workgroup 0 writes it
+  const int* cost_in;      // stage 2: that prefix
   // stage 1 that routes the tokens itself: logits in; the routing (as
   // moe_route_permute returns it) written out by workgroup 0.  E and top_k
   // count the shared expert when `shared` is 1: the logits then have E - 1
@@ -356,6 +392,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   const int k = lane / C, lc = lane & (C - 1);
   uint32_t* frags = lds;
   uint16_t* scales = reinterpret_cast<uint16_t*>(lds + kXE * NF * G * kFragDwords);
+  int* ucost = reinterpret_cast<int*>(scales + geo.wmax * unit_scale_halves(spb));
 
   // ---- routing: from the caller's arrays, or computed here (NPL > 0)
   int* ract = nullptr;     // LDS: active list, offsets, sorted slots
@@ -365,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   if constexpr (NPL > 0) {
     const int E = p.E, S = p.T * p.top_k;
     const int tid = threadIdx.x;
-    auto* rmask = reinterpret_cast<unsigned long long*>(scales + geo.wmax * unit_scale_halves(spb));
+    auto* rmask = reinterpret_cast<unsigned long long*>(ucost + geo.ucap);
     roff = reinterpret_cast<int*>(rmask + E);
     ract = roff + E + 1;
     rsorted = ract + E;
@@ -425,18 +462,43 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   auto offset_at = [&](int e) { if constexpr (NPL > 0) return roff[e]; else return p.offsets[e]; };
   auto sorted_at = [&](int r) { if constexpr (NPL > 0) return rsorted[r]; else return p.sorted_slots[r]; };
 
-  // This workgroup's share [u0, u1) of the units; in 32 bits when the
-  // products fit (a 64-bit division is a long instruction sequence that every
-  // wave runs before its first load).
-  int u0, u1;
-  if (geo.u32) {
-    const uint32_t U = static_cast<uint32_t>(n_active) * nb;
-    u0 = static_cast<int>(U * blockIdx.x / static_cast<uint32_t>(geo.nwg));
-    u1 = static_cast<int>(U * (blockIdx.x + 1) / static_cast<uint32_t>(geo.nwg));
+  int u0, u1;  // this workgroup's units
+  if (!geo.weighted) {
+    // in 32 bits when the products fit (a 64-bit division is a long
+    // instruction sequence that every wave runs before its first load)
+    const uint64_t U = static_cast<uint64_t>(n_active) * nb;
+    if (U * geo.nwg < (1ull << 32)) {
+      const uint32_t U32 = static_cast<uint32_t>(U);
+      u0 = static_cast<int>(U32 * blockIdx.x / static_cast<uint32_t>(geo.nwg));
+      u1 = static_cast<int>(U32 * (blockIdx.x + 1) / static_cast<uint32_t>(geo.nwg));
+    } else {
+      u0 = static_cast<int>(U * blockIdx.x / geo.nwg);
+      u1 = static_cast<int>(U * (blockIdx.x + 1) / geo.nwg);
+    }
   } else {
-    const int64_t U = static_cast<int64_t>(n_active) * nb;
-    u0 = static_cast<int>(U * blockIdx.x / geo.nwg);
-    u1 = static_cast<int>(U * (blockIdx.x + 1) / geo.nwg);
+    // Per-unit cost prefix of the active experts (see the units section):
+    // computed by the gate/up kernel, read back by the down kernel.
+    const int n_cost = n_active;
+    if constexpr (GATE_UP) {
+      const int a = threadIdx.x;  // n_active <= kThreads (E <= 1024 here, or S <= 512)
+      int c = 0;
+      if (a < n_cost) {
+        const int e = active_at(a);
+        c = unit_cost(offset_at(e + 1) - offset_at(e), NA);
+      }
+      int total;
+      const int ex = block_exclusive_scan(c, ucost + geo.ucap - (kScanThreads / 64 + 1), total);
+      if (a < n_cost) ucost[a] = ex;
+      if (a == 0) ucost[n_cost] = total;
+      if (blockIdx.x == 0 && a <= n_cost) p.cost_out[a] = a < n_cost ? ex : total;
+    } else {
+      for (int a = threadIdx.x; a <= n_cost; a += kThreads) ucost[a] = p.cost_in[a];
+    }
+    __syncthreads();
+    // the units that start in this workgroup's share of the cost
+    const int64_t ctot = static_cast<int64_t>(nb) * ucost[n_cost];
+    u0 = first_unit(ucost, n_cost, nb, ctot * blockIdx.x / geo.nwg);
+    u1 = first_unit(ucost, n_cost, nb, ctot * (blockIdx.x + 1) / geo.nwg);
   }
 
   for (int w0 = u0; w0 < u1;) {
@@ -541,10 +603,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
       if (threadIdx.x == 0) queue = w0 + kWaves;
       lds_barrier();
 
-      // compute side
-      float acc[NF];
+      // compute side: one accumulator per A row (stage 2 adds the row's hi
+      // and lo group dots, each unbiased on its own, before scaling)
+      float acc[NA];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) acc[f] = 0.f;
+      for (int m = 0; m < NA; ++m) acc[m] = 0.f;
       int cmc = 0, crf = 0, cscale = 0;
       int fb[NA];  // LDS dword offset of each A row's first fragment
 #pragma unroll
@@ -593,16 +656,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
             const Slot& sl = ring[d];
             const float z = static_cast<float>((sl.zw >> (4u * (crow & 7u))) & 0xFu);
             const Codes codes = expand_codes(sl.q);
-#pragma unroll
-            for (int f = 0; f < FPR; ++f) acc[f] = fmaf(scale, group_dot(codes, z, fp[f]), acc[f]);
+            {
+              float dsum = group_dot(codes, z, fp[0]);
+              if (FPR == 2) dsum += group_dot(codes, z, fp[FPR - 1]);
+              acc[0] = fmaf(scale, dsum, acc[0]);
+            }
 #pragma unroll
             for (int m = 1; m < NA; ++m)
               if (m < cmc) {
-#pragma unroll
-                for (int f = 0; f < FPR; ++f)
-                  acc[m * FPR + f] =
-                      fmaf(scale, group_dot(codes, z, read_frag(frags + fb[m] + (f * G + gg) * kFragDwords)),
-                           acc[m * FPR + f]);
+                float dsum = group_dot(codes, z, read_frag(frags + fb[m] + gg * kFragDwords));
+                if (FPR == 2)
+                  dsum += group_dot(codes, z, read_frag(frags + fb[m] + (G + gg) * kFragDwords));
+                acc[m] = fmaf(scale, dsum, acc[m]);
               }
             if (j == spb - 1) {  // block done: finish its rows
 #pragma unroll
@@ -621,14 +686,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
                       p.act_lo[idx] = lo;
                     }
                   } else {
-                    const float v = cluster_sum(acc[2 * m] + acc[2 * m + 1], C);
+                    const float v = cluster_sum(acc[m], C);
                     const int n = cb * R + k;
                     if (lc == 0 && n < H) p.y[static_cast<size_t>(crf + m) * H + n] = v;
                   }
                 }
               }
 #pragma unroll
-              for (int f = 0; f < NF; ++f) acc[f] = 0.f;
+              for (int m = 0; m < NA; ++m) acc[m] = 0.f;
             }
           }
           // Refill this slot with the next step; once the window is done this
@@ -659,11 +724,15 @@ size_t frag_bytes(const Geom& geo, int na) {
 // size, from the LDS a workgroup may hold.  Windows aim to cover a
 // workgroup's whole share of units, which is at most ceil(slots * nb / nwg).
 template <bool GATE_UP>
-int plan(Geom& geo, int T, int slots, const DeviceInfo& dev, size_t reserved) {
+int plan(Geom& geo, int T, int slots, const DeviceInfo& dev, size_t reserved, int rows_hint) {
   const size_t budget = static_cast<size_t>(dev.lds) - 256 - reserved;
   const size_t unit = static_cast<size_t>(unit_scale_halves(geo.spb)) * 2;
   const int want = static_cast<int>((static_cast<int64_t>(slots) * geo.nb + geo.nwg - 1) / geo.nwg) + 1;
+  // two rows per pass, or all rows of an expert known to hold up to 8 (a
+  // shared expert: T rows), so that its weights are streamed once; stage 2
+  // stops at 4 (eight rows of hi and lo fragments would spill registers)
   int na = T >= 2 ? 2 : 1;
+  if (rows_hint > 2) na = (GATE_UP && rows_hint > 4) ? 8 : 4;
   while (na > 1 && frag_bytes<GATE_UP>(geo, na) + unit * min(want, 16) > budget) na /= 2;
   const size_t fb = frag_bytes<GATE_UP>(geo, na);
   const size_t rest = budget > fb ? budget - fb : 0;
@@ -676,13 +745,26 @@ int plan(Geom& geo, int T, int slots, const DeviceInfo& dev, size_t reserved) {
 template <bool GATE_UP>
 size_t launch_lds(const Geom& geo, int na) {
   return frag_bytes<GATE_UP>(geo, na) +
-         static_cast<size_t>(geo.wmax) * unit_scale_halves(geo.spb) * 2;
+         static_cast<size_t>(geo.wmax) * unit_scale_halves(geo.spb) * 2 +
+         static_cast<size_t>(geo.ucap) * 4;
 }
+
+// Ints of the unit-cost table for `slots` active experts at most: the prefix
+// and the block scan's wave totals, rounded to 16 bytes.
+int cost_table_ints(int slots) { return (slots + 1 + kScanThreads / 64 + 1 + 3) & ~3; }
 
 template <bool GATE_UP, int NPL>
 void launch_decode_npl(const DecodeArgs& p, Geom geo, int na, size_t lds, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(geo.nwg)), block(kThreads);
-  if (na == 2)
+  if constexpr (GATE_UP) {
+    if (na == 8) {
+      hipLaunchKernelGGL((decode_kernel<GATE_UP, 8, NPL>), grid, block, lds, stream, p, geo);
+      return;
+    }
+  }
+  if (na == 4)
+    hipLaunchKernelGGL((decode_kernel<GATE_UP, 4, NPL>), grid, block, lds, stream, p, geo);
+  else if (na == 2)
     hipLaunchKernelGGL((decode_kernel<GATE_UP, 2, NPL>), grid, block, lds, stream, p, geo);
   else
     hipLaunchKernelGGL((decode_kernel<GATE_UP, 1, NPL>), grid, block, lds, stream, p, geo);
@@ -690,14 +772,17 @@ void launch_decode_npl(const DecodeArgs& p, Geom geo, int na, size_t lds, hipStr
 
 // route: stage 1 routes the tokens itself (p.logits, p.E <= 1024, T <= 64).
 template <bool GATE_UP>
-void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream, bool route) {
+void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream, bool route,
+                   int rows_hint) {
   // (p.E is set by every caller: the share arithmetic's width depends on it)
   const DeviceInfo dev = device_info();
   geo.nwg = dev.cus;
-  geo.u32 = static_cast<uint64_t>(p.E) * geo.nb * geo.nwg < (1ull << 32);
+  geo.weighted = rows_hint > 2;
+  geo.ucap = geo.weighted ? cost_table_ints(slots) : 0;
   const size_t rbytes = route ? route_lds_bytes(p.E, p.T * p.top_k) : 0;
-  const int na = plan<GATE_UP>(geo, p.T, slots, dev, rbytes);
-  const size_t lds = launch_lds<GATE_UP>(geo, na) + rbytes;
+  const int na =
+      plan<GATE_UP>(geo, p.T, slots, dev, rbytes + static_cast<size_t>(geo.ucap) * 4, rows_hint);
+  const size_t lds = launch_lds<GATE_UP>(geo, na) + rbytes;  // the cost table included
   if constexpr (GATE_UP) {
     if (route) {
       const int El = p.E - p.shared;  // logits per token
@@ -736,7 +821,8 @@ void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStrea
   p.E = a.E;
   p.act_hi = ws.act_hi;
   p.act_lo = ws.act_lo;
-  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, false);
+  p.cost_out = ws.tiles;  // the tile list region is free at decode sizes
+  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_hint);
 }
 
 bool route_in_gate_up(int64_t T, int E) { return T <= kDecodeMaxT && E <= 1024; }
@@ -760,6 +846,7 @@ void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const
   p.I = a.I;
   p.act_hi = ws.act_hi;
   p.act_lo = ws.act_lo;
+  p.cost_out = ws.tiles;
   p.logits = logits;
   p.E = a.E;
   p.shared = a.shared;
@@ -770,7 +857,7 @@ void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const
   p.r_slot_rows = r.slot_rows;
   p.r_active = r.active;
   p.r_num_active = r.num_active;
-  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, true);
+  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, true, a.rows_hint);
 }
 
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
@@ -794,7 +881,8 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
   p.I = a.I;
   p.E = a.E;
   p.y = a.y;
-  launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream, false);
+  p.cost_in = ws.tiles;  // written by the gate/up kernel
+  launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_hint);
 }
 
 }  // namespace moe
