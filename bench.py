@@ -55,7 +55,6 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 matrix, AMD published
 DEFAULT_WORKLOAD = "decode_e512_k10_h2560_i640_t8"
 PREFILL_WORKLOAD = "prefill_zipf_e512_k10_h2560_i640_t4096"
-DECODE_MAX_T = 8               # token counts at or below this run the GEMV kernels
 
 
 def log(msg: str) -> None:
@@ -82,6 +81,12 @@ def parse_args(argv=None):
     p.add_argument("--prefill-layers", type=int, default=4)
     p.add_argument("--no-block", action="store_true",
                    help="skip the block object (gate projection + shared expert)")
+    p.add_argument("--sweep", action="store_true",
+                   help="time every feasible plan (kernel variant and tile profile) at T = 1 ... "
+                        "4096 and I = 160 / 640 and print them, with the library's default")
+    p.add_argument("--sweep-tokens", default=None,
+                   help="comma-separated token counts for --sweep instead of "
+                        "1,2,4,8,9,16,32,64,128,1024,4096")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB a few times (counter calibration)")
     return p.parse_args(argv)
@@ -132,18 +137,33 @@ def layer_work(shape, num_active: int) -> dict:
     }
 
 
+def default_plan(shape):
+    from w4a16_group_quantized_amd import ops
+
+    return ops.plan_default(shape.T, shape.top_k, shape.E, shape.H, shape.I)
+
+
 def routed_decode(shape) -> bool:
     """The one-call layer routes inside its first kernel (moe_route_gate_up)."""
-    return shape.T <= DECODE_MAX_T and shape.E <= 1024
+    from w4a16_group_quantized_amd import ops
+
+    return default_plan(shape).route == ops.ROUTE_IN_GATE_UP
+
+
+def gemv_ffn(shape) -> bool:
+    """The layer's FFN runs the GEMV kernels (else the matrix-core GEMMs)."""
+    from w4a16_group_quantized_amd import ops
+
+    return default_plan(shape).ffn == ops.FFN_GEMV
 
 
 # --------------------------------------------------------------------------- #
 # HBM traffic and MFMA counters from committed rocprofv3 summaries
 # --------------------------------------------------------------------------- #
-def kernel_sources(T: int) -> list:
+def kernel_sources(gemv: bool) -> list:
     """Sources whose text fixes the kernels a workload's FFN runs."""
     csrc = "w4a16_group_quantized_amd/csrc/"
-    if T <= DECODE_MAX_T:
+    if gemv:
         return [csrc + "ffn_decode.hip", csrc + "common.h", csrc + "route.h", csrc + "permute.h"]
     return [csrc + "ffn_prefill.hip", csrc + "common.h"]
 
@@ -158,7 +178,7 @@ def source_sha256(rels: list) -> str:
     return h.hexdigest()
 
 
-def _summary_lines(workload: str, tag: str, name: str, T: int):
+def _summary_lines(workload: str, tag: str, name: str, gemv: bool):
     """key=value fields of line `<tag> <name> ...` in profiles/counters_<workload>.md,
     or None when absent or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
@@ -169,16 +189,16 @@ def _summary_lines(workload: str, tag: str, name: str, T: int):
         if len(parts) < 2 or parts[0] != tag or parts[1] != name:
             continue
         kv = dict(p.split("=", 1) for p in parts[2:])
-        if kv.get("source_sha256") != source_sha256(kernel_sources(T)):
+        if kv.get("source_sha256") != source_sha256(kernel_sources(gemv)):
             return None
         return kv
     return None
 
 
-def counter_traffic(workload: str, kernel: str, T: int):
+def counter_traffic(workload: str, kernel: str, gemv: bool):
     """HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
     scaled by what the counter reads for a plain copy of known size."""
-    kv = _summary_lines(workload, "traffic", kernel, T)
+    kv = _summary_lines(workload, "traffic", kernel, gemv)
     if kv is None:
         return None
     fetch = float(kv["fetch_kib"]) * float(kv["fetch_scale"]) * 1024
@@ -186,8 +206,8 @@ def counter_traffic(workload: str, kernel: str, T: int):
     return fetch + write
 
 
-def mfma_util(workload: str, kernel: str, T: int):
-    kv = _summary_lines(workload, "mfma", kernel, T)
+def mfma_util(workload: str, kernel: str, gemv: bool):
+    kv = _summary_lines(workload, "mfma", kernel, gemv)
     return None if kv is None else float(kv["util_pct"])
 
 
@@ -476,7 +496,7 @@ def measure_layer(args, shape, workload: str, host: dict, dev, counters_apply: b
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     ckey = "route_gate_up" if routed else "gate_up"
-    roof["traffic"] = counter_traffic(workload, ckey, shape.T) if counters_apply else None
+    roof["traffic"] = counter_traffic(workload, ckey, gemv_ffn(shape)) if counters_apply else None
     roof.update({
         "kernel": ("routed gate/up kernel (moe_route_gate_up: router, permutation and gate/up in "
                    "one launch, the first kernel of moe_layer_forward)" if routed
@@ -507,7 +527,8 @@ def measure_layer(args, shape, workload: str, host: dict, dev, counters_apply: b
             "down_kernel_us": down_ms * 1e3,
             "down_algorithmic_bytes": work["down_bytes"],
             "down_GBps": work["down_bytes"] / (down_ms * 1e-3) / 1e9,
-            "down_traffic": counter_traffic(workload, "down", shape.T) if counters_apply else None,
+            "down_traffic": (counter_traffic(workload, "down", gemv_ffn(shape)) if counters_apply
+                             else None),
         },
     }
 
@@ -568,7 +589,7 @@ def measure_prefill(args, workload: str, dev) -> dict:
     sub_ids[tokens], sub_w[tokens] = ids, wts
     ref = oracle.token_outputs(host, sub_ids, sub_w, tokens)
     err = error_figures(ref_out.cpu().numpy()[tokens], ref)
-    util = mfma_util(workload, "gate_up", shape.T)
+    util = mfma_util(workload, "gate_up", gemv_ffn(shape))
     return {
         "workload": workload,
         "T": shape.T, "E": shape.E, "top_k": shape.top_k, "H": shape.H, "I": shape.I,
@@ -658,6 +679,134 @@ def measure_block(args, shape, dev) -> dict:
 
 
 # --------------------------------------------------------------------------- #
+# the plan sweep behind the library's per-shape table
+# --------------------------------------------------------------------------- #
+SWEEP_T = (1, 2, 4, 8, 9, 16, 32, 64, 128, 1024, 4096)
+SWEEP_I = (160, 640)
+
+
+def candidate_plans(T: int, E: int, k: int, H: int, I: int) -> list:
+    """Every plan the library accepts for these sizes, among the variants swept."""
+    from w4a16_group_quantized_amd import ops
+
+    base = ops.plan_default(T, k, E, H, I).as_dict()
+    lanes = lambda G: [c for c in (1, 2, 4, 8) if G % c == 0]  # noqa: E731
+    out = []
+    if T <= 64:
+        gemv = dict(base, ffn=ops.FFN_GEMV, rows_per_pass=2 if T >= 2 else 1, cost_split=0)
+        # lanes per row, with either routing form
+        for route in ((ops.ROUTE_IN_GATE_UP, ops.ROUTE_ONE_LAUNCH) if E <= 1024
+                      else (ops.ROUTE_SEPARATE,)):
+            for lg in lanes(H // 32):
+                if lg < 2:
+                    continue
+                for ld in lanes(I // 32):
+                    out.append(dict(gemv, route=route, lanes_gate_up=lg, lanes_down=ld))
+        # rows per pass and the split of the work, with the default lanes
+        route = ops.ROUTE_IN_GATE_UP if E <= 1024 else ops.ROUTE_SEPARATE
+        for rows in (2, 4, 8):
+            if rows <= max(2, T):
+                for cost in (0, 1):
+                    out.append(dict(gemv, route=route, rows_per_pass=rows, cost_split=cost))
+    routes = (ops.ROUTE_ONE_LAUNCH, ops.ROUTE_SEPARATE) if T <= 64 and E <= 1024 else (
+        ops.ROUTE_SEPARATE,)
+    for msub in (1, 4):
+        for route in routes:
+            out.append(dict(base, ffn=ops.FFN_MFMA, route=route, msub=msub))
+    uniq = []
+    for d in out:
+        if d not in uniq:
+            uniq.append(d)
+    return base, uniq
+
+
+def _plan(d: dict):
+    from w4a16_group_quantized_amd import ops
+
+    p = ops.Plan()
+    for key, v in d.items():
+        setattr(p, key, v)
+    return p
+
+
+def run_sweep(args, dev) -> dict:
+    import numpy as np
+    import torch
+
+    from w4a16_group_quantized_amd import inputs as synth
+    from w4a16_group_quantized_amd import ops
+
+    rows = []
+    E, k, H = 512, 10, 2560
+    tokens = (tuple(int(t) for t in args.sweep_tokens.split(",")) if args.sweep_tokens
+              else SWEEP_T)
+    for I in SWEEP_I:
+        full = synth.MoEShape(E=E, top_k=k, H=H, I=I, T=max(tokens))
+        act = synth.make_activations(full, args.seed)  # smaller T: the first rows
+        w0 = ops.weights_to_device(synth.make_weights(full, args.seed), dev)
+        gw = torch.from_numpy(synth.make_gate_weight(full, args.seed)).to(dev)
+        n = 16
+        copies = device_copies(w0, n)
+        for T in tokens:
+            logits = torch.from_numpy(act["logits"][:T]).to(dev)
+            x = torch.from_numpy(np.ascontiguousarray(act["x"][:T])).to(dev)
+            ws = torch.empty(ops.layer_workspace_bytes(T, k, E, H, I), dtype=torch.uint8,
+                             device=dev)
+            out = torch.empty((T, H), dtype=torch.float16, device=dev)
+            steps = 64 if T <= 64 else (16 if T <= 1024 else 8)
+            base, plans = candidate_plans(T, E, k, H, I)
+            ref = None
+            for d in [base] + [p for p in plans if p != base]:
+                plan = _plan(d)
+
+                def step(i, plan=plan):
+                    ops.moe_layer_forward_plan(logits, x, k, copies[i % n], plan, ws, out)
+
+                step(0)
+                torch.cuda.synchronize()
+                got = out.clone()
+                if ref is None:
+                    ref = got
+                diff = float((got.float() - ref.float()).abs().max())
+                us = avg_ms(step, steps, 2) * 1e3
+                rows.append({"I": I, "T": T, "what": "layer", "plan": d, "default": d == base,
+                             "us": us, "max_abs_diff_vs_default": diff})
+                log(f"I={I} T={T} {'*' if d == base else ' '} {d}: {us:.1f} us (diff {diff:.2e})")
+            # the router projection alone: GEMV against matrix cores
+            if T <= 16:
+                logits_out = torch.empty((T, E), dtype=torch.float32, device=dev)
+                res = {}
+                for gemv in (1, 0):
+                    plan = _plan(dict(base, router_gemv=gemv))
+                    blk_ws = torch.empty(ops.block_workspace_bytes(T, k, E, False, H, I),
+                                         dtype=torch.uint8, device=dev)
+
+                    def bstep(i, plan=plan, blk_ws=blk_ws):
+                        ops.moe_block_forward_plan(x, gw, k, copies[i % n], False, plan, blk_ws,
+                                                   logits_out, out)
+
+                    res[gemv] = avg_ms(bstep, steps, 2) * 1e3
+                    rows.append({"I": I, "T": T, "what": "block (projection + layer)",
+                                 "plan": dict(base, router_gemv=gemv),
+                                 "default": gemv == base["router_gemv"], "us": res[gemv]})
+                log(f"I={I} T={T} block: router GEMV {res[1]:.1f} us, MFMA {res[0]:.1f} us")
+            del ws
+        del copies, w0
+        torch.cuda.empty_cache()
+    # per (I, T): the default plan against the fastest one swept
+    best = []
+    for I in SWEEP_I:
+        for T in tokens:
+            cand = [r for r in rows if r["I"] == I and r["T"] == T and r["what"] == "layer"]
+            d = [r for r in cand if r["default"]][0]
+            b = min(cand, key=lambda r: r["us"])
+            best.append({"I": I, "T": T, "default_us": d["us"], "best_us": b["us"],
+                         "default_over_best": d["us"] / b["us"], "best_plan": b["plan"],
+                         "default_plan": d["plan"]})
+    return {"sweep": rows, "summary": best}
+
+
+# --------------------------------------------------------------------------- #
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.copy_probe:
@@ -676,6 +825,12 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.sweep:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        ops.load_library()
+        print(json.dumps(run_sweep(args, dev)), flush=True)
+        return 0
     shape = synth.WORKLOADS[args.workload]
     if args.tokens is not None and args.tokens != shape.T:
         shape = dataclasses.replace(shape, T=args.tokens)
@@ -714,7 +869,7 @@ def main(argv=None) -> int:
         "layer": m["layer"],
     }
     gpu_out = m.pop("gpu_out")
-    decode = shape.T <= DECODE_MAX_T
+    decode = gemv_ffn(shape)
     torch.cuda.empty_cache()
     if decode and not args.no_block:
         result["block"] = measure_block(args, shape, dev)

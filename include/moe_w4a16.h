@@ -280,8 +280,9 @@ int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
  *   workspace        FFN workspace (moe_ffn_workspace_bytes); holds act for
  *                    moe_w4a16_down afterwards
  *
- * MOE_ERR_UNSUPPORTED unless T <= 8 and E <= 1024; other errors as the calls
- * it stands for.
+ * MOE_ERR_UNSUPPORTED unless T <= 64 and E <= 1024 (moe_layer_forward uses
+ * it up to 8 tokens, the default plan); other errors as the calls it stands
+ * for.
  */
 int moe_route_gate_up(const float* logits, const uint16_t* x, int64_t T,
                       int32_t E, int32_t top_k, const int32_t* w13_qweight,
@@ -383,6 +384,72 @@ int moe_block_forward(const uint16_t* x, int64_t T, const uint16_t* gate_weight,
                       int32_t H, int32_t I, int32_t group_size, float* logits,
                       uint16_t* out, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * Kernel variant and tile profile of a layer call.  Every entry point takes
+ * its choices from moe_plan_default for its sizes; the _plan entry points
+ * below take an explicit one (for measuring the alternatives).  The defaults
+ * were chosen from a sweep on MI355X ("[Perf][SM70] Narrow Qwen3.8 AWQ
+ * active grouped decode", section "Additional existing-autotune benefit
+ * (fresh-process pair)": the tuned tile per shape, there a W13 tile change
+ * from M64 x 128 x 32 to M8 x 256 x 64 at 4-8 tokens).
+ */
+#define MOE_FFN_GEMV 0            /* one weight stream per expert, A rows from LDS  */
+#define MOE_FFN_MFMA 1            /* matrix-core grouped GEMMs                      */
+#define MOE_ROUTE_IN_GATE_UP 0    /* the gate/up GEMV routes the tokens itself      */
+#define MOE_ROUTE_ONE_LAUNCH 1    /* router and permutation in one launch           */
+#define MOE_ROUTE_SEPARATE 2      /* router kernel, then the permutation kernels    */
+typedef struct moe_plan {
+  int32_t ffn;            /* MOE_FFN_GEMV or MOE_FFN_MFMA                            */
+  int32_t route;          /* MOE_ROUTE_*                                              */
+  int32_t msub;           /* MFMA: 32-row subtiles per M-tile, 1 or 4                 */
+  int32_t lanes_gate_up;  /* GEMV: lanes per w13 row, 1/2/4/8 dividing H/32           */
+  int32_t lanes_down;     /* GEMV: lanes per w2 row, 1/2/4/8 dividing I/32            */
+  int32_t rows_per_pass;  /* GEMV: A rows of an expert per weight pass, 1/2/4/8
+                             (the down stage takes at most 4)                         */
+  int32_t cost_split;     /* GEMV: 1 share work out by cost (rows per expert), 0 evenly */
+  int32_t router_gemv;    /* gate projection: 1 GEMV, 0 matrix cores                  */
+} moe_plan;
+
+/*
+ * moe_plan_default - the plan every entry point uses for these sizes (pure
+ * host function; `plan` is a HOST pointer).  top_k and E count the routed
+ * experts; shared = 1 for a layer with a shared expert (one more slot per
+ * token, one more expert, which holds all T rows).  MOE_ERR_INVALID_ARG /
+ * UNSUPPORTED for sizes the layer rejects.
+ */
+int moe_plan_default(int64_t T, int32_t top_k, int32_t E, int32_t shared, int32_t H,
+                     int32_t I, moe_plan* plan);
+
+/*
+ * moe_layer_forward_plan / moe_block_forward_plan - moe_layer_forward and
+ * moe_block_forward with an explicit plan (HOST pointer; NULL = the default).
+ * Every plan computes the same sums and the same routing; the order of the
+ * fp32 additions inside the FFN differs between GEMV and MFMA and with the
+ * lanes per row, so outputs may differ in the last bits.  Limits of a plan:
+ * GEMV and
+ * routing in gate/up or in one launch need T <= 64; routing in gate/up needs
+ * the GEMV and E (with the shared expert) <= 1024, and so does the one-launch
+ * router; the projection GEMV needs T <= 16 and T * H * 2 <= 80 KiB.
+ * MOE_ERR_INVALID_ARG for a malformed plan, MOE_ERR_UNSUPPORTED for one these
+ * sizes do not allow; nothing is enqueued then.
+ */
+int moe_layer_forward_plan(const float* logits, const uint16_t* x, int64_t T,
+                           int32_t E, int32_t top_k, const int32_t* w13_qweight,
+                           const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                           const int32_t* w2_qweight, const uint16_t* w2_scales,
+                           const int32_t* w2_qzeros, int32_t H, int32_t I,
+                           int32_t group_size, uint16_t* out, void* workspace,
+                           size_t workspace_bytes, const moe_plan* plan,
+                           void* stream);
+int moe_block_forward_plan(const uint16_t* x, int64_t T, const uint16_t* gate_weight,
+                           int32_t E, int32_t top_k, int32_t shared,
+                           const int32_t* w13_qweight, const uint16_t* w13_scales,
+                           const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                           const uint16_t* w2_scales, const int32_t* w2_qzeros,
+                           int32_t H, int32_t I, int32_t group_size, float* logits,
+                           uint16_t* out, void* workspace, size_t workspace_bytes,
+                           const moe_plan* plan, void* stream);
 
 /* Scratch bytes of moe_layer_forward_noalloc (per device). */
 #define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)

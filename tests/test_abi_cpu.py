@@ -132,7 +132,8 @@ def test_route_gate_up_rejects_bad_arguments():
         return lib.moe_route_gate_up(logits, FAKE, T, E, k, FAKE, FAKE, FAKE, H, I, gs, *p[:7],
                                      FAKE, ws_bytes, None)
 
-    assert call(T=9) == ops.MOE_ERR_UNSUPPORTED        # decode sizes only
+    assert call(T=65) == ops.MOE_ERR_UNSUPPORTED       # 64-token routing masks
+    assert call(T=9, ws_bytes=64) == ops.MOE_ERR_WORKSPACE  # 9..64 tokens are allowed
     assert call(E=1025) == ops.MOE_ERR_UNSUPPORTED
     assert call(gs=64) == ops.MOE_ERR_UNSUPPORTED
     assert call(ws_bytes=64) == ops.MOE_ERR_WORKSPACE

@@ -35,11 +35,14 @@ def test_layer_work_of_the_decode_workload():
     assert work["gate_up_flops"] == 4 * 8 * 10 * 2560 * 640
 
 
-def test_routed_decode_boundary():
-    """The one-call layer routes inside its first kernel at T <= 8 and E <= 1024."""
+def test_routed_decode_follows_the_library_plan():
+    """The one-call layer routes inside its first kernel where the plan table says so
+    (GEMV sizes, T <= 32, E <= 1024)."""
     base = synth.WORKLOADS["decode_e512_k10_h2560_i640_t8"]
-    assert bench.routed_decode(base)
-    assert not bench.routed_decode(synth.MoEShape(E=512, top_k=10, H=2560, I=640, T=9))
+    assert bench.routed_decode(base) and bench.gemv_ffn(base)
+    assert bench.routed_decode(synth.MoEShape(E=512, top_k=10, H=2560, I=640, T=32))
+    assert not bench.routed_decode(synth.MoEShape(E=512, top_k=10, H=2560, I=640, T=33))
+    assert not bench.gemv_ffn(synth.MoEShape(E=512, top_k=10, H=2560, I=640, T=33))
     assert not bench.routed_decode(synth.MoEShape(E=1025, top_k=10, H=2560, I=640, T=8))
     assert bench.routed_decode(synth.MoEShape(E=1024, top_k=10, H=2560, I=640, T=1))
 
@@ -48,22 +51,22 @@ def test_counter_lines_hold_only_for_their_sources(tmp_path, monkeypatch):
     """A traffic or MfmaUtil line is used only while the kernel sources hash as recorded."""
     import shutil
 
-    for rel in bench.kernel_sources(8):
+    for rel in bench.kernel_sources(True):
         dst = tmp_path / rel
         dst.parent.mkdir(parents=True, exist_ok=True)
         shutil.copy(os.path.join(ROOT, rel), dst)
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    sha = bench.source_sha256(bench.kernel_sources(8))
+    sha = bench.source_sha256(bench.kernel_sources(True))
     (tmp_path / "profiles").mkdir()
     (tmp_path / "profiles" / "counters_w.md").write_text(
         "text\n"
         f"traffic down fetch_kib=100 write_kib=10 fetch_scale=2 write_scale=1 source_sha256={sha}\n"
         f"mfma gate_up util_pct=31.5 source_sha256={sha}\n")
-    assert bench.counter_traffic("w", "down", 8) == (100 * 2 + 10) * 1024
-    assert bench.mfma_util("w", "gate_up", 8) == 31.5
-    assert bench.counter_traffic("w", "gate_up", 8) is None
-    (tmp_path / bench.kernel_sources(8)[0]).write_text("// changed\n")
-    assert bench.counter_traffic("w", "down", 8) is None
+    assert bench.counter_traffic("w", "down", True) == (100 * 2 + 10) * 1024
+    assert bench.mfma_util("w", "gate_up", True) == 31.5
+    assert bench.counter_traffic("w", "gate_up", True) is None
+    (tmp_path / bench.kernel_sources(True)[0]).write_text("// changed\n")
+    assert bench.counter_traffic("w", "down", True) is None
 
 
 def test_more_than_one_gpu_is_refused():

@@ -15,8 +15,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 LIB_NAME = "libmoe_w4a16.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "route_permute.hip", "router_gate.hip",
-           "ffn_decode.hip", "ffn_prefill.hip", "combine.hip"]
+SOURCES = ["abi.hip", "plan.hip", "route.hip", "permute.hip", "route_permute.hip",
+           "router_gate.hip", "ffn_decode.hip", "ffn_prefill.hip", "combine.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -31,8 +31,8 @@ int check_routing(int64_t T, int32_t top_k, int32_t E) {
 
 // The matrix-core variant addresses x with 32-bit byte offsets and numbers
 // its work items with int.
-int check_prefill(int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
-  if (T <= kDecodeMaxT) return MOE_OK;
+int check_mfma(const Plan& pl, int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
+  if (pl.ffn != MOE_FFN_MFMA) return MOE_OK;
   if (T * static_cast<int64_t>(H) >= (static_cast<int64_t>(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (prefill_max_items(T * top_k, E, H, I) >= (static_cast<int64_t>(1) << 31))
     return MOE_ERR_UNSUPPORTED;
@@ -52,6 +52,36 @@ int check_dims(int32_t H, int32_t I, int32_t group_size) {
   if (H <= 0 || I <= 0 || H % kGroup || I % kGroup) return MOE_ERR_INVALID_ARG;
   if (H / kGroup > kMaxGroups || I / kGroup > kMaxGroups) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// Enqueue the two halves of the FFN with the plan's variant (arguments
+// already validated).  Both halves of one FFN take the same plan: the
+// matrix-core down GEMM reads the tile list the gate/up call built.
+void run_gate_up(GateUpArgs a, const Plan& pl, void* workspace, hipStream_t st) {
+  const FfnWorkspace ws = ffn_workspace_carve(workspace, a.T, a.top_k, a.E, a.H, a.I);
+  a.lanes = pl.lanes_gate_up;
+  a.rows_per_pass = pl.rows_per_pass;
+  a.cost_split = pl.cost_split;
+  a.msub = pl.msub;
+  if (pl.ffn == MOE_FFN_GEMV) {
+    launch_gate_up_decode(a, ws, st);
+  } else {
+    launch_prefill_prep(a.x, a.T, a.H, a.I, a.offsets, a.active, a.num_active,
+                        static_cast<int64_t>(a.T) * a.top_k, a.E, pl.msub, ws, st);
+    launch_gate_up_prefill(a, ws, st);
+  }
+}
+
+void run_down(DownArgs d, const Plan& pl, void* workspace, hipStream_t st) {
+  const FfnWorkspace ws = ffn_workspace_carve(workspace, d.T, d.top_k, d.E, d.H, d.I);
+  d.lanes = pl.lanes_down;
+  d.rows_per_pass = pl.rows_per_pass;
+  d.cost_split = pl.cost_split;
+  d.msub = pl.msub;
+  if (pl.ffn == MOE_FFN_GEMV)
+    launch_down_decode(d, ws, st);
+  else
+    launch_down_prefill(d, ws, st);  // tile list from gate_up
 }
 
 }  // namespace
@@ -152,6 +182,7 @@ int moe_router_gate(const uint16_t* x, int64_t T, int32_t H, const uint16_t* gat
   if (T == 0) return MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(gate_weight) || !ok_ptr(logits)) return MOE_ERR_INVALID_ARG;
   launch_router_gate(x, static_cast<int>(T), H, gate_weight, E, logits,
+                     default_plan(T, 1, E, 0, H, kGroup).router_gemv != 0,
                      static_cast<hipStream_t>(stream));
   return check_launch();
 }
@@ -193,9 +224,11 @@ int moe_route_permute(const float* logits, int64_t T, int32_t E, int32_t top_k,
   const size_t need = permute_workspace_bytes(T, E);
   if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
   if (need > 0 && !ok_ptr(workspace)) return MOE_ERR_INVALID_ARG;
+  const bool one_launch =
+      default_plan(T, top_k, E, 0, kGroup, kGroup).route != MOE_ROUTE_SEPARATE;
   launch_route_permute(logits, static_cast<int>(T), E, top_k, 0, topk_ids, topk_weights,
                        expert_offsets, sorted_slots, slot_rows, active_experts, num_active,
-                       workspace, static_cast<hipStream_t>(stream));
+                       workspace, one_launch, static_cast<hipStream_t>(stream));
   return check_launch();
 }
 
@@ -212,14 +245,14 @@ int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t
                       void* stream) {
   if (int st = check_routing(T, top_k, E)) return st;
   if (int st = check_dims(H, I, group_size)) return st;
-  if (int st = check_prefill(T, top_k, E, H, I)) return st;
+  const Plan pl = default_plan(T, top_k, E, 0, H, I);
+  if (int st = check_mfma(pl, T, top_k, E, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(expert_offsets) || !ok_ptr(sorted_slots) || !ok_ptr(active_experts) ||
       !ok_ptr(num_active) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) || !ok_ptr(w13_qzeros) ||
       !ok_ptr(workspace))
     return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < ffn_workspace_bytes(T, top_k, E, H, I)) return MOE_ERR_WORKSPACE;
-  const FfnWorkspace ws = ffn_workspace_carve(workspace, T, top_k, E, H, I);
   GateUpArgs a;
   a.x = x;
   a.T = static_cast<int>(T);
@@ -234,13 +267,7 @@ int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t
   a.qw = w13_qweight;
   a.sc = w13_scales;
   a.qz = w13_qzeros;
-  if (T <= kDecodeMaxT) {
-    launch_gate_up_decode(a, ws, static_cast<hipStream_t>(stream));
-  } else {
-    launch_prefill_prep(x, static_cast<int>(T), H, I, expert_offsets, active_experts, num_active,
-                        T * top_k, E, ws, static_cast<hipStream_t>(stream));
-    launch_gate_up_prefill(a, ws, static_cast<hipStream_t>(stream));
-  }
+  run_gate_up(a, pl, workspace, static_cast<hipStream_t>(stream));
   return check_launch();
 }
 
@@ -253,7 +280,10 @@ int moe_route_gate_up(const float* logits, const uint16_t* x, int64_t T, int32_t
                       void* stream) {
   if (int st = check_routing(T, top_k, E)) return st;
   if (int st = check_dims(H, I, group_size)) return st;
-  if (!route_in_gate_up(T, E)) return MOE_ERR_UNSUPPORTED;
+  Plan pl = default_plan(T, top_k, E, 0, H, I);
+  pl.ffn = MOE_FFN_GEMV;
+  pl.route = MOE_ROUTE_IN_GATE_UP;
+  if (plan_check(pl, T, top_k, E, 0, H, I) != MOE_OK) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) ||
       !ok_ptr(w13_qzeros) || !ok_ptr(topk_ids) || !ok_ptr(topk_weights) ||
@@ -272,6 +302,9 @@ int moe_route_gate_up(const float* logits, const uint16_t* x, int64_t T, int32_t
   a.qw = w13_qweight;
   a.sc = w13_scales;
   a.qz = w13_qzeros;
+  a.lanes = pl.lanes_gate_up;
+  a.rows_per_pass = pl.rows_per_pass;
+  a.cost_split = pl.cost_split;
   const RouteOut r{topk_ids, topk_weights, expert_offsets, sorted_slots, slot_rows,
                    active_experts, num_active};
   launch_route_gate_up_decode(logits, a, r, ws, static_cast<hipStream_t>(stream));
@@ -285,14 +318,14 @@ int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
                    void* workspace, size_t workspace_bytes, void* stream) {
   if (int st = check_routing(T, top_k, E)) return st;
   if (int st = check_dims(H, I, group_size)) return st;
-  if (int st = check_prefill(T, top_k, E, H, I)) return st;
+  const Plan pl = default_plan(T, top_k, E, 0, H, I);
+  if (int st = check_mfma(pl, T, top_k, E, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(expert_offsets) || !ok_ptr(active_experts) || !ok_ptr(num_active) ||
       !ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) || !ok_ptr(y_sorted) ||
       !ok_ptr(workspace))
     return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < ffn_workspace_bytes(T, top_k, E, H, I)) return MOE_ERR_WORKSPACE;
-  const FfnWorkspace ws = ffn_workspace_carve(workspace, T, top_k, E, H, I);
   DownArgs a;
   a.T = static_cast<int>(T);
   a.top_k = top_k;
@@ -306,10 +339,7 @@ int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
   a.sc = w2_scales;
   a.qz = w2_qzeros;
   a.y = y_sorted;
-  if (T <= kDecodeMaxT)
-    launch_down_decode(a, ws, static_cast<hipStream_t>(stream));
-  else
-    launch_down_prefill(a, ws, static_cast<hipStream_t>(stream));  // tile list from gate_up
+  run_down(a, pl, workspace, static_cast<hipStream_t>(stream));
   return check_launch();
 }
 
@@ -401,19 +431,22 @@ size_t moe_layer_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t H,
   return layer_ws(nullptr, T, top_k, E, H, I).total;
 }
 
-// Sizes and pointers of a layer call (the shared expert, when `shared` is 1,
-// adds one slot per token and one expert); MOE_OK or the error to return.
+// Sizes, plan and pointers of a layer call (the shared expert, when `shared`
+// is 1, adds one slot per token and one expert); MOE_OK or the error to
+// return.  `pl` is the plan for top_k + shared slots and E + shared experts.
 static int layer_check(const float* logits, const uint16_t* x, int64_t T, int32_t E,
                        int32_t top_k, int32_t shared, const int32_t* w13_qweight,
                        const uint16_t* w13_scales, const int32_t* w13_qzeros,
                        const int32_t* w2_qweight, const uint16_t* w2_scales,
                        const int32_t* w2_qzeros, int32_t H, int32_t I, int32_t group_size,
-                       const uint16_t* out, const void* workspace, size_t workspace_bytes) {
+                       const uint16_t* out, const void* workspace, size_t workspace_bytes,
+                       const Plan& pl) {
   if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
   if (int st = check_routing(T, top_k, E)) return st;
   if (int st = check_routing(T, top_k + shared, E + shared)) return st;
   if (int st = check_dims(H, I, group_size)) return st;
-  if (int st = check_prefill(T, top_k + shared, E + shared, H, I)) return st;
+  if (int st = plan_check(pl, T, top_k, E, shared, H, I)) return st;
+  if (int st = check_mfma(pl, T, top_k + shared, E + shared, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) ||
       !ok_ptr(w13_qzeros) || !ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) ||
@@ -428,60 +461,68 @@ static int layer_check(const float* logits, const uint16_t* x, int64_t T, int32_
 // the routing gives every token one more slot, (expert E, weight 1), and the
 // permutation, the FFN and the combine run over E + 1 experts and top_k + 1
 // slots, so the shared expert's rows go through the same launches as the
-// routed experts' rows.
+// routed experts' rows (its default plan takes all its T rows in one pass
+// and shares the GEMV work out by cost).
 static int layer_run(const float* logits, const uint16_t* x, int64_t T, int32_t E, int32_t top_k,
                      int32_t shared, const int32_t* w13_qweight, const uint16_t* w13_scales,
                      const int32_t* w13_qzeros, const int32_t* w2_qweight,
                      const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t H, int32_t I,
-                     int32_t group_size, uint16_t* out, void* workspace, void* stream) {
+                     uint16_t* out, void* workspace, const Plan& pl, void* stream) {
   if (T == 0) return MOE_OK;
   const int32_t kk = top_k + shared, EP = E + shared;
   const LayerWs w = layer_ws(workspace, T, kk, EP, H, I);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (route_in_gate_up(T, EP)) {
-    // decode: the gate/up kernel routes the tokens itself
+  GateUpArgs a{};
+  a.x = x;
+  a.T = static_cast<int>(T);
+  a.top_k = kk;
+  a.E = EP;
+  a.shared = shared;
+  a.H = H;
+  a.I = I;
+  a.offsets = w.offsets;
+  a.sorted_slots = w.sorted;
+  a.active = w.active;
+  a.num_active = w.num_active;
+  a.qw = w13_qweight;
+  a.sc = w13_scales;
+  a.qz = w13_qzeros;
+  DownArgs d{};
+  d.T = static_cast<int>(T);
+  d.top_k = kk;
+  d.E = EP;
+  d.H = H;
+  d.I = I;
+  d.offsets = w.offsets;
+  d.active = w.active;
+  d.num_active = w.num_active;
+  d.qw = w2_qweight;
+  d.sc = w2_scales;
+  d.qz = w2_qzeros;
+  d.y = w.y;
+  if (pl.route == MOE_ROUTE_IN_GATE_UP) {
+    // the gate/up GEMV routes the tokens itself
     const FfnWorkspace fws = ffn_workspace_carve(w.ffn, T, kk, EP, H, I);
-    GateUpArgs a{};
-    a.x = x;
-    a.T = static_cast<int>(T);
-    a.top_k = kk;
-    a.E = EP;
-    a.shared = shared;
-    a.rows_hint = shared ? static_cast<int>(T) : 0;
-    a.H = H;
-    a.I = I;
-    a.qw = w13_qweight;
-    a.sc = w13_scales;
-    a.qz = w13_qzeros;
+    a.lanes = pl.lanes_gate_up;
+    a.rows_per_pass = pl.rows_per_pass;
+    a.cost_split = pl.cost_split;
     const RouteOut r{w.ids, w.weights, w.offsets, w.sorted, w.slot_rows, w.active, w.num_active};
     launch_route_gate_up_decode(logits, a, r, fws, st);
-    DownArgs d{};
-    d.T = static_cast<int>(T);
-    d.top_k = kk;
-    d.E = EP;
-    d.rows_hint = a.rows_hint;
-    d.H = H;
-    d.I = I;
-    d.offsets = w.offsets;
-    d.active = w.active;
-    d.num_active = w.num_active;
-    d.qw = w2_qweight;
-    d.sc = w2_scales;
-    d.qz = w2_qzeros;
-    d.y = w.y;
-    launch_down_decode(d, fws, st);
   } else {
     launch_route_permute(logits, static_cast<int>(T), E, top_k, shared, w.ids, w.weights,
-                         w.offsets, w.sorted, w.slot_rows, w.active, w.num_active, w.perm, st);
-    if (int e = check_launch()) return e;
-    if (int e = moe_w4a16_grouped_ffn(x, T, kk, w.offsets, w.sorted, w.active, w.num_active,
-                                      w13_qweight, w13_scales, w13_qzeros, w2_qweight, w2_scales,
-                                      w2_qzeros, EP, H, I, group_size, w.y, w.ffn, w.ffn_bytes,
-                                      stream))
-      return e;
+                         w.offsets, w.sorted, w.slot_rows, w.active, w.num_active, w.perm,
+                         pl.route == MOE_ROUTE_ONE_LAUNCH, st);
+    run_gate_up(a, pl, w.ffn, st);
   }
+  run_down(d, pl, w.ffn, st);
   launch_combine(w.y, w.weights, w.slot_rows, static_cast<int>(T), kk, H, out, st);
   return check_launch();
+}
+
+// The plan to use: the caller's, or the default for the layer's sizes.
+static Plan layer_plan(const moe_plan* plan, int64_t T, int32_t top_k, int32_t E, int32_t shared,
+                       int32_t H, int32_t I) {
+  return plan ? *plan : default_plan(T, top_k, E, shared, H, I);
 }
 
 static int layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t E,
@@ -489,13 +530,26 @@ static int layer_forward(const float* logits, const uint16_t* x, int64_t T, int3
                          const uint16_t* w13_scales, const int32_t* w13_qzeros,
                          const int32_t* w2_qweight, const uint16_t* w2_scales,
                          const int32_t* w2_qzeros, int32_t H, int32_t I, int32_t group_size,
-                         uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+                         uint16_t* out, void* workspace, size_t workspace_bytes,
+                         const moe_plan* plan, void* stream) {
+  const Plan pl = layer_plan(plan, T, top_k, E, shared, H, I);
   if (int st = layer_check(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
                            w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace,
-                           workspace_bytes))
+                           workspace_bytes, pl))
     return st;
   return layer_run(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
-                   w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace, stream);
+                   w2_qweight, w2_scales, w2_qzeros, H, I, out, workspace, pl, stream);
+}
+
+int moe_plan_default(int64_t T, int32_t top_k, int32_t E, int32_t shared, int32_t H, int32_t I,
+                     moe_plan* plan) {
+  if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
+  if (int st = check_routing(T, top_k, E)) return st;
+  if (int st = check_routing(T, top_k + shared, E + shared)) return st;
+  if (int st = check_dims(H, I, kGroup)) return st;
+  if (plan == nullptr) return MOE_ERR_INVALID_ARG;
+  *plan = default_plan(T, top_k, E, shared, H, I);
+  return MOE_OK;
 }
 
 int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t E, int32_t top_k,
@@ -506,7 +560,18 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int64_t T, int32_t
                       void* stream) {
   return layer_forward(logits, x, T, E, top_k, 0, w13_qweight, w13_scales, w13_qzeros,
                        w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, nullptr, stream);
+}
+
+int moe_layer_forward_plan(const float* logits, const uint16_t* x, int64_t T, int32_t E,
+                           int32_t top_k, const int32_t* w13_qweight, const uint16_t* w13_scales,
+                           const int32_t* w13_qzeros, const int32_t* w2_qweight,
+                           const uint16_t* w2_scales, const int32_t* w2_qzeros, int32_t H,
+                           int32_t I, int32_t group_size, uint16_t* out, void* workspace,
+                           size_t workspace_bytes, const moe_plan* plan, void* stream) {
+  return layer_forward(logits, x, T, E, top_k, 0, w13_qweight, w13_scales, w13_qzeros,
+                       w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace,
+                       workspace_bytes, plan, stream);
 }
 
 size_t moe_block_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t shared, int32_t H,
@@ -518,6 +583,29 @@ size_t moe_block_workspace_bytes(int64_t T, int32_t top_k, int32_t E, int32_t sh
   return layer_ws(nullptr, T, top_k + shared, E + shared, H, I).total;
 }
 
+int moe_block_forward_plan(const uint16_t* x, int64_t T, const uint16_t* gate_weight, int32_t E,
+                           int32_t top_k, int32_t shared, const int32_t* w13_qweight,
+                           const uint16_t* w13_scales, const int32_t* w13_qzeros,
+                           const int32_t* w2_qweight, const uint16_t* w2_scales,
+                           const int32_t* w2_qzeros, int32_t H, int32_t I, int32_t group_size,
+                           float* logits, uint16_t* out, void* workspace, size_t workspace_bytes,
+                           const moe_plan* plan, void* stream) {
+  // everything is checked before the projection is enqueued
+  if (int st = check_router_gate(T, H, E)) return st;
+  const Plan pl = layer_plan(plan, T, top_k, E, shared, H, I);
+  if (int st = layer_check(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
+                           w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace,
+                           workspace_bytes, pl))
+    return st;
+  if (T == 0) return MOE_OK;
+  if (!ok_ptr(gate_weight)) return MOE_ERR_INVALID_ARG;
+  launch_router_gate(x, static_cast<int>(T), H, gate_weight, E, logits, pl.router_gemv != 0,
+                     static_cast<hipStream_t>(stream));
+  if (int e = check_launch()) return e;
+  return layer_run(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
+                   w2_qweight, w2_scales, w2_qzeros, H, I, out, workspace, pl, stream);
+}
+
 int moe_block_forward(const uint16_t* x, int64_t T, const uint16_t* gate_weight, int32_t E,
                       int32_t top_k, int32_t shared, const int32_t* w13_qweight,
                       const uint16_t* w13_scales, const int32_t* w13_qzeros,
@@ -525,19 +613,9 @@ int moe_block_forward(const uint16_t* x, int64_t T, const uint16_t* gate_weight,
                       const int32_t* w2_qzeros, int32_t H, int32_t I, int32_t group_size,
                       float* logits, uint16_t* out, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  // everything is checked before the projection is enqueued
-  if (int st = check_router_gate(T, H, E)) return st;
-  if (int st = layer_check(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
-                           w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace,
-                           workspace_bytes))
-    return st;
-  if (T == 0) return MOE_OK;
-  if (!ok_ptr(gate_weight)) return MOE_ERR_INVALID_ARG;
-  launch_router_gate(x, static_cast<int>(T), H, gate_weight, E, logits,
-                     static_cast<hipStream_t>(stream));
-  if (int e = check_launch()) return e;
-  return layer_run(logits, x, T, E, top_k, shared, w13_qweight, w13_scales, w13_qzeros,
-                   w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, workspace, stream);
+  return moe_block_forward_plan(x, T, gate_weight, E, top_k, shared, w13_qweight, w13_scales,
+                                w13_qzeros, w2_qweight, w2_scales, w2_qzeros, H, I, group_size,
+                                logits, out, workspace, workspace_bytes, nullptr, stream);
 }
 
 }  // extern "C"
@@ -592,5 +670,5 @@ extern "C" int moe_layer_forward_noalloc(const float* logits, const uint16_t* x,
   if (ws == nullptr) return err;
   return layer_forward(logits, x, T, E, top_k, 0, w13_qweight, w13_scales, w13_qzeros,
                        w2_qweight, w2_scales, w2_qzeros, H, I, group_size, out, ws,
-                       MOE_NOALLOC_SCRATCH_BYTES, stream);
+                       MOE_NOALLOC_SCRATCH_BYTES, nullptr, stream);
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/moe_w4a16.h"
+
 namespace moe {
 
 constexpr int kGroup = 32;          // quantisation group size along K
@@ -12,7 +14,6 @@ constexpr int kMaxExperts = 4096;   // E limit
 constexpr int kMaxTopK = 64;        // top_k limit (one router round per lane)
 constexpr int kMaxGroups = 512;     // K / 32 limit (K <= 16384)
 constexpr int kPermBlockTokens = 64;  // tokens per permutation block (one 64-bit mask)
-constexpr int kDecodeMaxT = 8;      // T at or below which the GEMV variant runs
 constexpr int kMaxDevices = 64;     // devices with cached attributes
 
 // Compute-unit count and the LDS bytes one workgroup may use on the current
@@ -24,6 +25,13 @@ struct DeviceInfo {
   int lds;
 };
 DeviceInfo device_info();
+
+// Kernel variant and tile profile (plan.hip): the default for given sizes,
+// and whether an explicit plan is allowed for them (MOE_OK or an error code).
+// top_k and E count the routed experts; shared = 1 adds a shared expert.
+using Plan = moe_plan;
+Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I);
+int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, int I);
 
 // ----------------------------------------------------------------------------
 // Launchers (each enqueues on `stream`, returns nothing; the ABI layer checks
@@ -39,18 +47,20 @@ void launch_permute(const int* ids, int T, int top_k, int E, int* offsets,
                     int* sorted_slots, int* slot_rows, int* active,
                     int* num_active, void* workspace, hipStream_t stream);
 
-// Router and permutation in one call: one launch when route_permute_fused(T,
-// E + shared) (small T), else the two launches above.  E is the logits'
-// expert count; with shared = 1 the permutation covers E + 1 experts and
-// top_k + 1 slots per token.
-bool route_permute_fused(int64_t T, int E);
+// Router and permutation in one call: one launch when `one_launch` (T <= 64,
+// E + shared <= 1024), else the router kernel and the permutation kernels.
+// E is the logits' expert count; with shared = 1 the permutation covers
+// E + 1 experts and top_k + 1 slots per token.
 void launch_route_permute(const float* logits, int T, int E, int top_k, int shared, int* ids,
                           float* weights, int* offsets, int* sorted_slots, int* slot_rows,
-                          int* active, int* num_active, void* workspace, hipStream_t stream);
+                          int* active, int* num_active, void* workspace, bool one_launch,
+                          hipStream_t stream);
 
-// Router gate projection logits[T, E] = x[T, H] . Wg[E, H]^T (router_gate.hip).
+// Router gate projection logits[T, E] = x[T, H] . Wg[E, H]^T (router_gate.hip):
+// the GEMV variant when `gemv` (T <= 16, T * H * 2 <= 80 KiB), else the
+// matrix-core one.
 void launch_router_gate(const uint16_t* x, int T, int H, const uint16_t* gate_weight, int E,
-                        float* logits, hipStream_t stream);
+                        float* logits, bool gemv, hipStream_t stream);
 
 struct FfnWorkspace {
   uint16_t* act_hi;  // [S, I] fp16, high part of SiLU(gate)*up
@@ -68,7 +78,10 @@ struct GateUpArgs {
   const uint16_t* x;
   int T, top_k, E, H, I;
   int shared = 0;  // routing kernels only: top_k and E count a shared expert (index E - 1)
-  int rows_hint = 0;  // decode: an expert may hold this many rows (a shared expert holds T)
+  int lanes = 0;          // GEMV: lanes per weight row (from the plan)
+  int rows_per_pass = 0;  // GEMV: A rows of an expert per weight pass (from the plan)
+  int cost_split = 0;     // GEMV: units shared out by cost (from the plan)
+  int msub = 0;           // MFMA: 32-row subtiles per M-tile (from the plan)
   const int* offsets;
   const int* sorted_slots;
   const int* active;
@@ -79,7 +92,10 @@ struct GateUpArgs {
 };
 struct DownArgs {
   int T, top_k, E, H, I;
-  int rows_hint = 0;  // as in GateUpArgs
+  int lanes = 0;  // as in GateUpArgs
+  int rows_per_pass = 0;
+  int cost_split = 0;
+  int msub = 0;
   const int* offsets;
   const int* active;
   const int* num_active;
@@ -91,9 +107,9 @@ struct DownArgs {
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 
 // Stage 1 of the decode FFN that first routes the T tokens itself, from
-// logits [T, E] (route_in_gate_up(T, E): T <= kDecodeMaxT, E <= 1024), and
-// writes the routing out as moe_route_permute does.  The routing fields of
-// `a` (offsets, sorted_slots, active, num_active) are not read.
+// logits [T, E] (T <= 64, E <= 1024), and writes the routing out as
+// moe_route_permute does.  The routing fields of `a` (offsets, sorted_slots,
+// active, num_active) are not read.
 struct RouteOut {
   int* ids;
   float* weights;
@@ -103,19 +119,16 @@ struct RouteOut {
   int* active;
   int* num_active;
 };
-bool route_in_gate_up(int64_t T, int E);
 void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const RouteOut& r,
                                  const FfnWorkspace& ws, hipStream_t stream);
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 
-// Matrix-core variant: a prep kernel (tile list built from the routing, x
-// permuted to k-slot order, both into the FFN workspace) followed by the two
-// grouped GEMMs.  prefill_msub is the number of 32-row subtiles per M-tile
-// for S = T * top_k sorted rows over E experts.
-int prefill_msub(int64_t S, int E);
+// Matrix-core variant: a prep kernel (tile list of M-tiles of msub 32-row
+// subtiles built from the routing, x permuted to k-slot order, both into the
+// FFN workspace) followed by the two grouped GEMMs, which take the same msub.
 int64_t prefill_max_items(int64_t S, int E, int H, int I);   // grid of the larger GEMM
 void launch_prefill_prep(const uint16_t* x, int T, int H, int I, const int* offsets,
-                         const int* active, const int* num_active, int64_t S, int E,
+                         const int* active, const int* num_active, int64_t S, int E, int msub,
                          const FfnWorkspace& ws, hipStream_t stream);
 void launch_gate_up_prefill(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 void launch_down_prefill(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);

@@ -707,12 +707,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
 }
 
 // ----------------------------------------------------------------- host -----
-// Lanes per row: the largest power of two <= 8 that divides G.
-int cluster_lanes(int G) {
-  int C = 1;
-  while (C < 8 && G % (2 * C) == 0) C *= 2;
-  return C;
-}
 
 // LDS bytes of the A fragments: kXE experts x na rows (stage 2: hi and lo).
 template <bool GATE_UP>
@@ -724,15 +718,13 @@ size_t frag_bytes(const Geom& geo, int na) {
 // size, from the LDS a workgroup may hold.  Windows aim to cover a
 // workgroup's whole share of units, which is at most ceil(slots * nb / nwg).
 template <bool GATE_UP>
-int plan(Geom& geo, int T, int slots, const DeviceInfo& dev, size_t reserved, int rows_hint) {
+int plan(Geom& geo, int slots, const DeviceInfo& dev, size_t reserved, int rows_per_pass) {
   const size_t budget = static_cast<size_t>(dev.lds) - 256 - reserved;
   const size_t unit = static_cast<size_t>(unit_scale_halves(geo.spb)) * 2;
   const int want = static_cast<int>((static_cast<int64_t>(slots) * geo.nb + geo.nwg - 1) / geo.nwg) + 1;
-  // two rows per pass, or all rows of an expert known to hold up to 8 (a
-  // shared expert: T rows), so that its weights are streamed once; stage 2
-  // stops at 4 (eight rows of hi and lo fragments would spill registers)
-  int na = T >= 2 ? 2 : 1;
-  if (rows_hint > 2) na = (GATE_UP && rows_hint > 4) ? 8 : 4;
+  // the plan's rows per pass; stage 2 stops at 4 (eight rows of hi and lo
+  // fragments would spill registers), and fewer when LDS is short
+  int na = GATE_UP ? rows_per_pass : min(rows_per_pass, 4);
   while (na > 1 && frag_bytes<GATE_UP>(geo, na) + unit * min(want, 16) > budget) na /= 2;
   const size_t fb = frag_bytes<GATE_UP>(geo, na);
   const size_t rest = budget > fb ? budget - fb : 0;
@@ -773,15 +765,15 @@ void launch_decode_npl(const DecodeArgs& p, Geom geo, int na, size_t lds, hipStr
 // route: stage 1 routes the tokens itself (p.logits, p.E <= 1024, T <= 64).
 template <bool GATE_UP>
 void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream, bool route,
-                   int rows_hint) {
+                   int rows_per_pass, int cost_split) {
   // (p.E is set by every caller: the share arithmetic's width depends on it)
   const DeviceInfo dev = device_info();
   geo.nwg = dev.cus;
-  geo.weighted = rows_hint > 2;
+  geo.weighted = cost_split && slots <= kThreads;  // the cost scan: one expert per thread
   geo.ucap = geo.weighted ? cost_table_ints(slots) : 0;
   const size_t rbytes = route ? route_lds_bytes(p.E, p.T * p.top_k) : 0;
   const int na =
-      plan<GATE_UP>(geo, p.T, slots, dev, rbytes + static_cast<size_t>(geo.ucap) * 4, rows_hint);
+      plan<GATE_UP>(geo, slots, dev, rbytes + static_cast<size_t>(geo.ucap) * 4, rows_per_pass);
   const size_t lds = launch_lds<GATE_UP>(geo, na) + rbytes;  // the cost table included
   if constexpr (GATE_UP) {
     if (route) {
@@ -801,7 +793,7 @@ void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream,
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
   Geom geo{};
   geo.G = a.H / kGroup;
-  geo.C = cluster_lanes(geo.G);
+  geo.C = a.lanes;  // a power of two <= 8 dividing G (the plan)
   geo.spb = geo.G / geo.C;
   const int half = (64 / geo.C) / 2;  // gate (= up) rows per block
   geo.nb = (a.I + half - 1) / half;
@@ -822,16 +814,14 @@ void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStrea
   p.act_hi = ws.act_hi;
   p.act_lo = ws.act_lo;
   p.cost_out = ws.tiles;  // the tile list region is free at decode sizes
-  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_hint);
+  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_per_pass, a.cost_split);
 }
-
-bool route_in_gate_up(int64_t T, int E) { return T <= kDecodeMaxT && E <= 1024; }
 
 void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const RouteOut& r,
                                  const FfnWorkspace& ws, hipStream_t stream) {
   Geom geo{};
   geo.G = a.H / kGroup;
-  geo.C = cluster_lanes(geo.G);
+  geo.C = a.lanes;
   geo.spb = geo.G / geo.C;
   const int half = (64 / geo.C) / 2;
   geo.nb = (a.I + half - 1) / half;
@@ -857,13 +847,13 @@ void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const
   p.r_slot_rows = r.slot_rows;
   p.r_active = r.active;
   p.r_num_active = r.num_active;
-  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, true, a.rows_hint);
+  launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, true, a.rows_per_pass, a.cost_split);
 }
 
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
   Geom geo{};
   geo.G = a.I / kGroup;
-  geo.C = cluster_lanes(geo.G);
+  geo.C = a.lanes;
   geo.spb = geo.G / geo.C;
   geo.nb = (a.H + 64 / geo.C - 1) / (64 / geo.C);
   DecodeArgs p{};
@@ -882,7 +872,7 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
   p.E = a.E;
   p.y = a.y;
   p.cost_in = ws.tiles;  // written by the gate/up kernel
-  launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_hint);
+  launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_per_pass, a.cost_split);
 }
 
 }  // namespace moe

@@ -636,13 +636,6 @@ __global__ __launch_bounds__(1024) void prefill_prep_kernel(
   }
 }
 
-int tile_rows(int64_t S, int E) { return prefill_msub(S, E) * kSub; }
-
-int64_t max_tiles(int64_t S, int E) {
-  const int bm = tile_rows(S, E);
-  return (S + bm - 1) / bm + std::min<int64_t>(E, S);
-}
-
 // Workgroups per range.  An item of s live subtiles costs
 // c = kSubCost s + kItemBase, at least c1 = kSubCost + kItemBase and at most
 // c1 s, so a range (1/8 of the cost) holds at most 1/8 of the items'
@@ -671,27 +664,24 @@ int ntiles_down(int H) { return (H + kBN - 1) / kBN; }
 
 }  // namespace
 
-int prefill_msub(int64_t S, int E) { return S >= 64 * static_cast<int64_t>(E) ? 4 : 1; }
-
 int64_t prefill_max_items(int64_t S, int E, int H, int I) {
   return 8 * range_bound(S, E, std::max(ntiles_gate_up(I), ntiles_down(H)));
 }
 
 void launch_prefill_prep(const uint16_t* x, int T, int H, int I, const int* offsets,
-                         const int* active, const int* num_active, int64_t S, int E,
+                         const int* active, const int* num_active, int64_t S, int E, int msub,
                          const FfnWorkspace& ws, hipStream_t stream) {
   const int64_t chunks = static_cast<int64_t>(T) * H / 8;
   const unsigned blocks = 1 + static_cast<unsigned>((chunks + 1023) / 1024);
   hipLaunchKernelGGL(prefill_prep_kernel, dim3(blocks), dim3(1024), 0, stream, offsets, active,
-                     num_active, tile_rows(S, E), kSubCost, kItemBase, ntiles_gate_up(I),
+                     num_active, msub * kSub, kSubCost, kItemBase, ntiles_gate_up(I),
                      ntiles_down(H), ws.tiles, ws.tile_count, ws.sched, x, ws.x_perm, chunks);
 }
 
 void launch_gate_up_prefill(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
   PrefillArgs p{ws.x_perm, nullptr, a.sorted_slots, a.T, a.top_k, a.E, a.H, a.I, a.offsets,
                 ws.tiles, ws.tile_count, a.qw, a.sc, a.qz, ws.act_hi, ws.act_lo, nullptr};
-  const int64_t S = static_cast<int64_t>(a.T) * a.top_k;
-  if (prefill_msub(S, a.E) == 4)
+  if (a.msub == 4)  // the prep kernel's tiles are of a.msub subtiles too
     launch_gemm<true, 4>(p, ntiles_gate_up(a.I), ws.sched, stream);
   else
     launch_gemm<true, 1>(p, ntiles_gate_up(a.I), ws.sched, stream);
@@ -700,9 +690,8 @@ void launch_gate_up_prefill(const GateUpArgs& a, const FfnWorkspace& ws, hipStre
 void launch_down_prefill(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
   PrefillArgs p{ws.act_hi, ws.act_lo, nullptr, a.T, a.top_k, a.E, a.H, a.I, a.offsets,
                 ws.tiles, ws.tile_count, a.qw, a.sc, a.qz, nullptr, nullptr, a.y};
-  const int64_t S = static_cast<int64_t>(a.T) * a.top_k;
   const int* sched = ws.sched + kSchedStride;
-  if (prefill_msub(S, a.E) == 4)
+  if (a.msub == 4)
     launch_gemm<false, 4>(p, ntiles_down(a.H), sched, stream);
   else
     launch_gemm<false, 1>(p, ntiles_down(a.H), sched, stream);

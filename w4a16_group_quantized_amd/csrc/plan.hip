@@ -1,0 +1,113 @@
+// Per-shape choice of kernel variant and tile profile: the one table every
+// entry point takes its choices from ("[Perf][SM70] Narrow Qwen3.8 AWQ active
+// grouped decode", section "Additional existing-autotune benefit
+// (fresh-process pair)": tuned tiles per shape, there a W13 tile change from
+// M64 x 128 x 32 to M8 x 256 x 64 at 4-8 tokens).  Host code only, a pure
+// function of the sizes.  The entries below were chosen from a sweep of the
+// layer on MI355X at T = 1 ... 4096 and I = 160 / 640 (bench.py --sweep),
+// every plan timed on 16 weight copies.
+#include "../../include/moe_w4a16.h"
+#include "common.h"
+
+namespace moe {
+
+// The table.  Layer times at 512 experts, top-10, hidden 2560 from the
+// sweep, in us: the fastest GEMV plan and the fastest matrix-core plan.
+//   tokens          1     8     9    16    32    64   | I
+//   GEMV          30.2  70.2  76.3 113.2 182.5 298.3  | 640
+//   MFMA          45.0  88.2 102.9 141.1 212.3 307.4  | 640
+//   GEMV          26.4  39.8  43.1  54.3  78.2 122.1  | 160
+//   MFMA          39.2  51.0  52.2  65.2  83.9 116.3  | 160
+// GEMV (one weight stream, A rows from LDS) up to 32 tokens, the matrix-core
+// GEMMs above.
+constexpr int64_t kGemvMaxT = 32;
+// Routing inside the gate/up GEMV (every workgroup routes the T tokens
+// itself) is the fastest GEMV form at every size swept.
+constexpr int64_t kRouteInKernelMaxT = kGemvMaxT;
+constexpr int kRouteInKernelMaxE = 1024;
+// Router and permutation as one single-workgroup launch: faster than the two
+// kernels up to 8 tokens only (its 16 waves route the tokens in turn).
+constexpr int64_t kRouteOneLaunchMaxT = 8;
+constexpr int kRouteOneLaunchMaxE = 1024;
+// From 10 tokens some expert draws 3 or more rows: four A rows per weight
+// pass and work shared out by cost (I = 640, 10 tokens: 119.8 us with two
+// rows and an even split, 82.5 us with four and the cost split).
+constexpr int64_t kRows4MinT = 10;
+// 128-row M-tiles (4 subtiles) once an expert averages 64 rows or more
+// (I = 640: 1024 tokens 529.9 us with 32-row tiles, 593.0 with 128;
+// 4096 skewed tokens 1226.8 us with 128-row tiles, 1384.3 with 32).
+constexpr int64_t kMsub4RowsPerExpert = 64;
+// Router projection: GEMV up to 16 tokens with x (T x H fp16) in 80 KiB of
+// LDS (block at 8 tokens, I = 640: 78.6 us with it, 94.4 us with MFMA).
+constexpr int64_t kRouterGemvMaxT = 16;
+constexpr int64_t kRouterGemvMaxXBytes = 80 * 1024;
+
+// Lanes per weight row of a GEMV over K = 32 G: the largest power of two
+// <= 8 that divides G (a lane takes every lanes-th group of the row).
+static int gemv_lanes(int G) {
+  int C = 1;
+  while (C < 8 && G % (2 * C) == 0) C *= 2;
+  return C;
+}
+
+// Smallest power of two >= n, at most 8.
+static int pow2_rows(int64_t n) {
+  int r = 1;
+  while (r < 8 && r < n) r *= 2;
+  return r;
+}
+
+Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
+  Plan p;
+  const int kk = top_k + shared, EP = E + shared;  // slots per token, experts
+  const int64_t S = T * static_cast<int64_t>(kk);
+  p.ffn = T <= kGemvMaxT ? MOE_FFN_GEMV : MOE_FFN_MFMA;
+  if (p.ffn == MOE_FFN_GEMV && T <= kRouteInKernelMaxT && EP <= kRouteInKernelMaxE)
+    p.route = MOE_ROUTE_IN_GATE_UP;
+  else if (T <= kRouteOneLaunchMaxT && EP <= kRouteOneLaunchMaxE)
+    p.route = MOE_ROUTE_ONE_LAUNCH;
+  else
+    p.route = MOE_ROUTE_SEPARATE;
+  p.msub = S >= kMsub4RowsPerExpert * static_cast<int64_t>(EP) ? 4 : 1;
+  p.lanes_gate_up = gemv_lanes(H / kGroup);
+  p.lanes_down = gemv_lanes(I / kGroup);
+  // A shared expert holds all T rows: take them (up to 8) in one pass and
+  // share the work out by cost.
+  if (shared) {
+    p.rows_per_pass = pow2_rows(T);
+    p.cost_split = T > 2;
+  } else {
+    p.rows_per_pass = T >= kRows4MinT ? 4 : (T >= 2 ? 2 : 1);
+    p.cost_split = T >= kRows4MinT;
+  }
+  p.router_gemv = T <= kRouterGemvMaxT && T * static_cast<int64_t>(H) * 2 <= kRouterGemvMaxXBytes;
+  return p;
+}
+
+int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, int I) {
+  (void)top_k;
+  E += shared;
+  if (p.ffn != MOE_FFN_GEMV && p.ffn != MOE_FFN_MFMA) return MOE_ERR_INVALID_ARG;
+  if (p.rows_per_pass != 1 && p.rows_per_pass != 2 && p.rows_per_pass != 4 &&
+      p.rows_per_pass != 8)
+    return MOE_ERR_INVALID_ARG;
+  if (p.cost_split != 0 && p.cost_split != 1) return MOE_ERR_INVALID_ARG;
+  if (p.route < MOE_ROUTE_IN_GATE_UP || p.route > MOE_ROUTE_SEPARATE) return MOE_ERR_INVALID_ARG;
+  if (p.msub != 1 && p.msub != 4) return MOE_ERR_INVALID_ARG;
+  auto lanes_ok = [](int c, int G) { return (c == 1 || c == 2 || c == 4 || c == 8) && G % c == 0; };
+  if (!lanes_ok(p.lanes_gate_up, H / kGroup) || !lanes_ok(p.lanes_down, I / kGroup))
+    return MOE_ERR_INVALID_ARG;
+  if (p.router_gemv != 0 && p.router_gemv != 1) return MOE_ERR_INVALID_ARG;
+  // what each variant supports (the table above picks within these limits)
+  if (p.ffn == MOE_FFN_GEMV && T > kPermBlockTokens) return MOE_ERR_UNSUPPORTED;
+  if (p.route == MOE_ROUTE_IN_GATE_UP &&
+      (p.ffn != MOE_FFN_GEMV || T > kPermBlockTokens || E > kRouteInKernelMaxE))
+    return MOE_ERR_UNSUPPORTED;
+  if (p.route == MOE_ROUTE_ONE_LAUNCH && (T > kPermBlockTokens || E > kRouteOneLaunchMaxE))
+    return MOE_ERR_UNSUPPORTED;
+  if (p.router_gemv && (T > kRouterGemvMaxT || T * static_cast<int64_t>(H) * 2 > kRouterGemvMaxXBytes))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -92,13 +92,11 @@ void launch_fused(const float* logits, int T, int E, int top_k, int shared, int*
 
 }  // namespace
 
-// E counts the permutation's experts (the shared one included).
-bool route_permute_fused(int64_t T, int E) { return T <= kPermBlockTokens && E <= kFusedMaxE; }
-
 void launch_route_permute(const float* logits, int T, int E, int top_k, int shared, int* ids,
                           float* weights, int* offsets, int* sorted_slots, int* slot_rows,
-                          int* active, int* num_active, void* workspace, hipStream_t stream) {
-  if (!route_permute_fused(T, E + shared)) {
+                          int* active, int* num_active, void* workspace, bool one_launch,
+                          hipStream_t stream) {
+  if (!one_launch) {
     launch_route(logits, T, E, top_k, shared, ids, weights, stream);
     launch_permute(ids, T, top_k + shared, E + shared, offsets, sorted_slots, slot_rows, active,
                    num_active, workspace, stream);

@@ -6,7 +6,7 @@
 // 2560 as in "[Model][SM70] Adapt Qwen3.8 Flash Next NVFP4", section
 // "Implemented route").
 //
-// Few tokens (T <= kGemvMaxT, decode): the work is reading Wg once (2.6 MB at
+// Few tokens (T <= 16, decode): the work is reading Wg once (2.6 MB at
 // 512 x 2560), so it is a GEMV bound by HBM.  One wave per expert row: lane l
 // takes the row's 16-byte chunks l, l + 64, ..., all issued before x is
 // staged; x (T rows) sits in LDS; v_dot2_f32_f16 multiplies fp16 pairs
@@ -212,13 +212,9 @@ __global__ __launch_bounds__(kMmThreads) void router_mfma_kernel(
 
 }  // namespace
 
-bool router_gate_gemv(int64_t T, int H) {
-  return T <= kGemvMaxT && static_cast<int64_t>(T) * H * 2 <= 80 * 1024;
-}
-
 void launch_router_gate(const uint16_t* x, int T, int H, const uint16_t* gate_weight, int E,
-                        float* logits, hipStream_t stream) {
-  if (router_gate_gemv(T, H)) {
+                        float* logits, bool gemv, hipStream_t stream) {
+  if (gemv) {  // T <= kGemvMaxT and x in 80 KiB of LDS (the plan checks it)
     const dim3 grid((E + kGemvWaves - 1) / kGemvWaves);
     const size_t lds = static_cast<size_t>(T) * H * 2;
     hipLaunchKernelGGL(router_gemv_kernel, grid, dim3(64 * kGemvWaves), lds, stream, x, T, H,

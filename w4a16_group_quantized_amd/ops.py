@@ -45,7 +45,28 @@ EXPORTED = (
     "moe_route_shared",
     "moe_block_workspace_bytes",
     "moe_block_forward",
+    "moe_plan_default",
+    "moe_layer_forward_plan",
+    "moe_block_forward_plan",
 )
+
+FFN_GEMV, FFN_MFMA = 0, 1
+ROUTE_IN_GATE_UP, ROUTE_ONE_LAUNCH, ROUTE_SEPARATE = 0, 1, 2
+
+
+class Plan(ctypes.Structure):
+    """moe_plan: kernel variant and tile profile of a layer call."""
+
+    _fields_ = [("ffn", ctypes.c_int32), ("route", ctypes.c_int32), ("msub", ctypes.c_int32),
+                ("lanes_gate_up", ctypes.c_int32), ("lanes_down", ctypes.c_int32),
+                ("rows_per_pass", ctypes.c_int32), ("cost_split", ctypes.c_int32),
+                ("router_gemv", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+    def __repr__(self):
+        return f"Plan({self.as_dict()})"
 
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -100,6 +121,15 @@ _SIGNATURES = {
     "moe_router_gate": (ctypes.c_int, [_P, _I64, _I32, _P, _I32, _P, _P]),
     "moe_route_shared": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "moe_block_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32]),
+    "moe_plan_default": (ctypes.c_int, [_I64, _I32, _I32, _I32, _I32, _I32, _P]),
+    "moe_layer_forward_plan": (
+        ctypes.c_int,
+        [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P,
+         _P]),
+    "moe_block_forward_plan": (
+        ctypes.c_int,
+        [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P,
+         _SZ, _P, _P]),
     "moe_block_forward": (
         ctypes.c_int,
         [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P,
@@ -421,6 +451,53 @@ def moe_block_forward(x: torch.Tensor, gate_weight: torch.Tensor, top_k: int, w:
         _ptr(w["w13_z"]), _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]), H, I, GROUP_SIZE,
         _ptr(logits), _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
     return out, logits
+
+
+def plan_default(T: int, top_k: int, E: int, H: int, I: int, shared: bool = False) -> Plan:
+    """The plan the library uses for these sizes (routed top_k and E; `shared`: a shared expert)."""
+    p = Plan()
+    _check("moe_plan_default", load_library().moe_plan_default(T, top_k, E, int(shared), H, I,
+                                                               ctypes.addressof(p)))
+    return p
+
+
+def _plan_ptr(plan):
+    return None if plan is None else ctypes.addressof(plan)
+
+
+def moe_layer_forward_plan(logits: torch.Tensor, x: torch.Tensor, top_k: int, w: dict,
+                           plan: Plan | None, workspace: torch.Tensor | None = None,
+                           out: torch.Tensor | None = None):
+    """moe_layer_forward with an explicit plan (None: the default)."""
+    lib = load_library()
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w["w2_q"].shape[2] * 8
+    dev = x.device
+    if workspace is None:
+        workspace = _workspace(layer_workspace_bytes(T, top_k, E, H, I), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float16, device=dev)
+    _check("moe_layer_forward_plan", lib.moe_layer_forward_plan(
+        _ptr(logits), _ptr(x), T, E, top_k, _ptr(w["w13_q"]), _ptr(w["w13_s"]), _ptr(w["w13_z"]),
+        _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]), H, I, GROUP_SIZE, _ptr(out),
+        _ptr(workspace), workspace.numel(), _plan_ptr(plan), _stream()))
+    return out
+
+
+def moe_block_forward_plan(x: torch.Tensor, gate_weight: torch.Tensor, top_k: int, w: dict,
+                           shared: bool, plan: Plan | None, workspace: torch.Tensor,
+                           logits: torch.Tensor, out: torch.Tensor):
+    """moe_block_forward with an explicit plan (None: the default)."""
+    lib = load_library()
+    T, H = x.shape
+    E = gate_weight.shape[0]
+    I = w["w2_q"].shape[2] * 8
+    _check("moe_block_forward_plan", lib.moe_block_forward_plan(
+        _ptr(x), T, _ptr(gate_weight), E, top_k, int(shared), _ptr(w["w13_q"]), _ptr(w["w13_s"]),
+        _ptr(w["w13_z"]), _ptr(w["w2_q"]), _ptr(w["w2_s"]), _ptr(w["w2_z"]), H, I, GROUP_SIZE,
+        _ptr(logits), _ptr(out), _ptr(workspace), workspace.numel(), _plan_ptr(plan), _stream()))
+    return out
 
 
 class MoEBlock:
