@@ -26,9 +26,9 @@ Measurement
     their output bit for bit.
   * roofline: the first FFN kernel of the timed step (decode: the routed
     gate/up kernel of moe_route_gate_up; prefill: the gate/up call), launched
-    alone back to back on the routing of the batch, timed with HIP events on
-    its stream; achieved = its algorithmic bytes (or flops) per launch / its
-    average launch time.  layer_hbm_frac (top level) is the whole step's
+    alone K times back to back on the routing of the batch, HIP events on its
+    stream around the K launches; achieved = its algorithmic bytes (or flops)
+    per launch / the average launch time.  layer_hbm_frac (top level) is the whole step's
     algorithmic bytes / step time / 8 TB/s.
   * cpu_baseline: the CPU oracle (test infrastructure) timed on this host on
     the same workload, best of a few repeats, with max |err| and relative RMS
@@ -303,6 +303,26 @@ def avg_ms(fn, steps: int, warm: int = 4) -> float:
     return a.elapsed_time(b) / steps
 
 
+def per_launch_ms(fn, steps: int, warm: int = 4) -> float:
+    """Mean over `steps` launches of the time between HIP events recorded just
+    before and just after each fn(i) on the current stream: the kernel's own
+    duration plus its dispatch, without the gaps between launches."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        fn(i)
+    evs = [_events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
 def graph_timings(step, copies: int, steps: int, warmup: int, check):
     """(per-step graph ms, graph-of-`copies`-steps ms per step): step(c) captured once per
     weight copy and replayed round-robin, then all `copies` steps captured as one graph.
@@ -426,20 +446,32 @@ def measure_layer(args, shape, workload: str, host: dict, dev, counters_apply: b
         ", ".join(f"{k} {v:.1f}" for k, v in segments.items()) + " us")
     assert torch.equal(layer.out, ref_out), "eager steps disagree"
 
-    # the first FFN kernel alone, back to back on the batch's routing, each
-    # launch on the next weight copy
+    # the first FFN kernel alone on the batch's routing, each launch on the
+    # next weight copy: HIP events around every launch (the roofline's time),
+    # and back to back
     if routed:
-        gate_up_ms = avg_ms(lambda i: ops.moe_route_gate_up(
-            logits, x, shape.top_k, copies[i % args.layers], layer.ids, layer.weights, layer.perm,
-            layer.ffn_ws), args.steps)
+        def gate_up_call(i):
+            ops.moe_route_gate_up(logits, x, shape.top_k, copies[i % args.layers], layer.ids,
+                                  layer.weights, layer.perm, layer.ffn_ws)
     else:
-        gate_up_ms = avg_ms(lambda i: ops.moe_w4a16_gate_up(
-            x, shape.top_k, layer.perm, copies[i % args.layers], layer.ffn_ws), args.steps)
-    down_ms = avg_ms(lambda i: ops.moe_w4a16_down(
-        shape.T, shape.top_k, layer.perm, copies[i % args.layers], layer.y_sorted, layer.ffn_ws),
-        args.steps)
-    log(f"back-to-back: {'routed ' if routed else ''}gate_up {gate_up_ms * 1e3:.1f} us, "
-        f"down {down_ms * 1e3:.1f} us")
+        def gate_up_call(i):
+            ops.moe_w4a16_gate_up(x, shape.top_k, layer.perm, copies[i % args.layers],
+                                  layer.ffn_ws)
+
+    def down_call(i):
+        ops.moe_w4a16_down(shape.T, shape.top_k, layer.perm, copies[i % args.layers],
+                           layer.y_sorted, layer.ffn_ws)
+
+    # back to back is the roofline's time: an event pair around each launch
+    # adds its own dispatch (about 2 us here), the gaps between back-to-back
+    # launches of one stream are smaller
+    gate_up_ms = avg_ms(gate_up_call, args.steps)
+    down_ms = avg_ms(down_call, args.steps)
+    gate_up_1_ms = per_launch_ms(gate_up_call, args.steps)
+    down_1_ms = per_launch_ms(down_call, args.steps)
+    log(f"back to back: {'routed ' if routed else ''}gate_up {gate_up_ms * 1e3:.1f} us, down "
+        f"{down_ms * 1e3:.1f} us (events around each launch {gate_up_1_ms * 1e3:.1f} / "
+        f"{down_1_ms * 1e3:.1f} us)")
 
     # the timed step: one moe_layer_forward call, bit for bit the separate calls
     def layer_step(i: int):
@@ -502,6 +534,8 @@ def measure_layer(args, shape, workload: str, host: dict, dev, counters_apply: b
                    "one launch, the first kernel of moe_layer_forward)" if routed
                    else "gate/up call (moe_w4a16_gate_up: tile-list prep + gate/up GEMM)"),
         "avg_launch_us": gate_up_ms * 1e3,
+        "timing": "HIP events around K back-to-back launches on the kernel's stream, / K",
+        "events_around_each_launch_us": gate_up_1_ms * 1e3,
         "algorithmic_bytes_per_launch": gu_bytes,
         "algorithmic_flops_per_launch": work["gate_up_flops"],
     })
@@ -525,6 +559,7 @@ def measure_layer(args, shape, workload: str, host: dict, dev, counters_apply: b
             "mfma_frac": work["flops"] / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
             "segments_us": segments,
             "down_kernel_us": down_ms * 1e3,
+            "down_events_around_each_launch_us": down_1_ms * 1e3,
             "down_algorithmic_bytes": work["down_bytes"],
             "down_GBps": work["down_bytes"] / (down_ms * 1e-3) / 1e9,
             "down_traffic": (counter_traffic(workload, "down", gemv_ffn(shape)) if counters_apply
@@ -571,10 +606,10 @@ def measure_prefill(args, workload: str, dev) -> dict:
     graph_ms, multi_ms = graph_timings(layer_step, n, steps, 2, check)
     timing, ms = pick_timing({"eager": eager_ms, "hip-graph replay": graph_ms,
                               f"hip-graph replay of {n} layer steps": multi_ms}, steps, n)
-    gate_up_ms = avg_ms(lambda i: ops.moe_w4a16_gate_up(x, shape.top_k, layer.perm, copies[i % n],
-                                                        layer.ffn_ws), steps, 2)
-    down_ms = avg_ms(lambda i: ops.moe_w4a16_down(shape.T, shape.top_k, layer.perm, copies[i % n],
-                                                  layer.y_sorted, layer.ffn_ws), steps, 2)
+    gate_up_ms = per_launch_ms(lambda i: ops.moe_w4a16_gate_up(
+        x, shape.top_k, layer.perm, copies[i % n], layer.ffn_ws), steps, 2)
+    down_ms = per_launch_ms(lambda i: ops.moe_w4a16_down(
+        shape.T, shape.top_k, layer.perm, copies[i % n], layer.y_sorted, layer.ffn_ws), steps, 2)
     work = layer_work(shape, int(layer.perm["num_active"].item()))
     tflops = work["flops"] / (ms * 1e-3) / 1e12
     gu_tflops = work["gate_up_flops"] / (gate_up_ms * 1e-3) / 1e12
@@ -649,8 +684,8 @@ def measure_block(args, shape, dev) -> dict:
         graph_ms, multi_ms = graph_timings(step, n, args.steps, args.warmup, check)
     timing, ms = pick_timing({"eager": eager_ms, "hip-graph replay": graph_ms,
                               f"hip-graph replay of {n} layer steps": multi_ms}, args.steps, n)
-    proj_ms = avg_ms(lambda i: ops.moe_router_gate(x, copies[i % n]["gate_w"], blk.logits),
-                     args.steps)
+    proj_ms = per_launch_ms(lambda i: ops.moe_router_gate(x, copies[i % n]["gate_w"], blk.logits),
+                            args.steps)
     num_active = int(blk.views()["num_active"].item())  # the shared expert included
     w13, w2 = expert_bytes(shape.H, shape.I)
     proj_bytes = shape.E * shape.H * 2 + shape.T * shape.H * 2 + shape.T * shape.E * 4
