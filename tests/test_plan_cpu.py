@@ -120,3 +120,16 @@ def test_layer_rejects_plans_the_sizes_do_not_allow():
     assert _layer(lib, dict(plan(8, E=1025), route=ops.ROUTE_IN_GATE_UP), E=1025) == \
         ops.MOE_ERR_UNSUPPORTED
     assert _layer(lib, dict(plan(17), router_gemv=1), T=17) == ops.MOE_ERR_UNSUPPORTED
+
+
+def test_gemv_that_does_not_fit_lds_falls_back_or_is_refused():
+    """At I = 16384 the down GEMV's A fragments alone need 160 KiB of LDS: the
+    default plan takes the matrix cores, and an explicit GEMV plan is refused
+    before anything is enqueued."""
+    small = plan(8, E=8, k=2, H=256, I=15360)
+    big = plan(8, E=8, k=2, H=256, I=16384)
+    assert small["ffn"] == ops.FFN_GEMV
+    assert big["ffn"] == ops.FFN_MFMA and big["route"] == ops.ROUTE_ONE_LAUNCH
+    lib = ops.load_library()
+    forced = dict(big, ffn=ops.FFN_GEMV, route=ops.ROUTE_IN_GATE_UP)
+    assert _layer(lib, forced, T=8, E=8, k=2, H=256, I=16384) == ops.MOE_ERR_UNSUPPORTED

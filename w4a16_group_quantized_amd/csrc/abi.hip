@@ -29,6 +29,15 @@ int check_routing(int64_t T, int32_t top_k, int32_t E) {
   return MOE_OK;
 }
 
+// A GEMV plan must fit the device's LDS per workgroup (checked before
+// anything is enqueued).
+int check_gemv(const Plan& pl, int64_t T, int32_t top_k, int32_t E, int32_t shared, int32_t H,
+               int32_t I) {
+  if (pl.ffn != MOE_FFN_GEMV) return MOE_OK;
+  const size_t lds = static_cast<size_t>(device_info().lds);
+  return gemv_fits(pl, T, top_k, E, shared, H, I, lds) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
 // The matrix-core variant addresses x with 32-bit byte offsets and numbers
 // its work items with int.
 int check_mfma(const Plan& pl, int64_t T, int32_t top_k, int32_t E, int32_t H, int32_t I) {
@@ -247,6 +256,7 @@ int moe_w4a16_gate_up(const uint16_t* x, int64_t T, int32_t top_k, const int32_t
   if (int st = check_dims(H, I, group_size)) return st;
   const Plan pl = default_plan(T, top_k, E, 0, H, I);
   if (int st = check_mfma(pl, T, top_k, E, H, I)) return st;
+  if (int st = check_gemv(pl, T, top_k, E, 0, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(x) || !ok_ptr(expert_offsets) || !ok_ptr(sorted_slots) || !ok_ptr(active_experts) ||
       !ok_ptr(num_active) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) || !ok_ptr(w13_qzeros) ||
@@ -284,6 +294,7 @@ int moe_route_gate_up(const float* logits, const uint16_t* x, int64_t T, int32_t
   pl.ffn = MOE_FFN_GEMV;
   pl.route = MOE_ROUTE_IN_GATE_UP;
   if (plan_check(pl, T, top_k, E, 0, H, I) != MOE_OK) return MOE_ERR_UNSUPPORTED;
+  if (int st = check_gemv(pl, T, top_k, E, 0, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) ||
       !ok_ptr(w13_qzeros) || !ok_ptr(topk_ids) || !ok_ptr(topk_weights) ||
@@ -320,6 +331,7 @@ int moe_w4a16_down(int64_t T, int32_t top_k, const int32_t* expert_offsets,
   if (int st = check_dims(H, I, group_size)) return st;
   const Plan pl = default_plan(T, top_k, E, 0, H, I);
   if (int st = check_mfma(pl, T, top_k, E, H, I)) return st;
+  if (int st = check_gemv(pl, T, top_k, E, 0, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(expert_offsets) || !ok_ptr(active_experts) || !ok_ptr(num_active) ||
       !ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) || !ok_ptr(y_sorted) ||
@@ -447,6 +459,7 @@ static int layer_check(const float* logits, const uint16_t* x, int64_t T, int32_
   if (int st = check_dims(H, I, group_size)) return st;
   if (int st = plan_check(pl, T, top_k, E, shared, H, I)) return st;
   if (int st = check_mfma(pl, T, top_k + shared, E + shared, H, I)) return st;
+  if (int st = check_gemv(pl, T, top_k, E, shared, H, I)) return st;
   if (T == 0) return MOE_OK;
   if (!ok_ptr(logits) || !ok_ptr(x) || !ok_ptr(w13_qweight) || !ok_ptr(w13_scales) ||
       !ok_ptr(w13_qzeros) || !ok_ptr(w2_qweight) || !ok_ptr(w2_scales) || !ok_ptr(w2_qzeros) ||

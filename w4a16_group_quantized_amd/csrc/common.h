@@ -32,6 +32,9 @@ DeviceInfo device_info();
 using Plan = moe_plan;
 Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I);
 int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, int I);
+// Whether a GEMV plan's kernels fit `lds_bytes` of LDS per workgroup.
+bool gemv_fits(const Plan& p, int64_t T, int top_k, int E, int shared, int H, int I,
+               size_t lds_bytes);
 
 // ----------------------------------------------------------------------------
 // Launchers (each enqueues on `stream`, returns nothing; the ABI layer checks
@@ -122,6 +125,13 @@ struct RouteOut {
 void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const RouteOut& r,
                                  const FfnWorkspace& ws, hipStream_t stream);
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
+
+// Least LDS bytes one workgroup of a GEMV stage needs at these sizes and
+// lanes per row (ffn_decode.hip); a plan whose GEMV needs more than the
+// device gives a workgroup cannot run.
+size_t gemv_min_lds(bool gate_up, bool route, int64_t T, int top_k, int E, int H, int I,
+                    int lanes, bool cost_split);
+constexpr size_t kGfx950LdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 
 // Matrix-core variant: a prep kernel (tile list of M-tiles of msub 32-row
 // subtiles built from the routing, x permuted to k-slot order, both into the

@@ -45,6 +45,8 @@
 // bias removed on its own, and the two are added before the group's scale.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "permute.h"
 #include "route.h"
@@ -789,6 +791,22 @@ void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream,
 }
 
 }  // namespace
+
+// The least LDS a GEMV stage can run with: one A row per pass, one unit per
+// window, plus the routing and cost tables it keeps.
+size_t gemv_min_lds(bool gate_up, bool route, int64_t T, int top_k, int E, int H, int I,
+                    int lanes, bool cost_split) {
+  Geom geo{};
+  geo.G = (gate_up ? H : I) / kGroup;
+  geo.C = lanes;
+  geo.spb = geo.G / geo.C;
+  const int slots = static_cast<int>(std::min<int64_t>(E, T * top_k));
+  const size_t frags = gate_up ? frag_bytes<true>(geo, 1) : frag_bytes<false>(geo, 1);
+  size_t need = frags + static_cast<size_t>(unit_scale_halves(geo.spb)) * 2 + 256;
+  if (route) need += route_lds_bytes(E, static_cast<int>(T * top_k));
+  if (cost_split && slots <= kThreads) need += static_cast<size_t>(cost_table_ints(slots)) * 4;
+  return need;
+}
 
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
   Geom geo{};

@@ -57,6 +57,9 @@ static int pow2_rows(int64_t n) {
   return r;
 }
 
+bool gemv_fits(const Plan& p, int64_t T, int top_k, int E, int shared, int H, int I,
+               size_t lds_bytes);
+
 Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
   Plan p;
   const int kk = top_k + shared, EP = E + shared;  // slots per token, experts
@@ -81,7 +84,23 @@ Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
     p.cost_split = T >= kRows4MinT;
   }
   p.router_gemv = T <= kRouterGemvMaxT && T * static_cast<int64_t>(H) * 2 <= kRouterGemvMaxXBytes;
+  // the GEMV's A fragments of a long K (I near 16384 for the down stage)
+  // do not fit a workgroup's LDS: the matrix cores then take every size
+  if (p.ffn == MOE_FFN_GEMV && !gemv_fits(p, T, top_k, E, shared, H, I, kGfx950LdsBytes)) {
+    p.ffn = MOE_FFN_MFMA;
+    if (p.route == MOE_ROUTE_IN_GATE_UP)
+      p.route = T <= kRouteOneLaunchMaxT && EP <= kRouteOneLaunchMaxE ? MOE_ROUTE_ONE_LAUNCH
+                                                                      : MOE_ROUTE_SEPARATE;
+  }
   return p;
+}
+
+bool gemv_fits(const Plan& p, int64_t T, int top_k, int E, int shared, int H, int I,
+               size_t lds_bytes) {
+  const int kk = top_k + shared, EP = E + shared;
+  const bool route = p.route == MOE_ROUTE_IN_GATE_UP;
+  return gemv_min_lds(true, route, T, kk, EP, H, I, p.lanes_gate_up, p.cost_split) <= lds_bytes &&
+         gemv_min_lds(false, false, T, kk, EP, H, I, p.lanes_down, p.cost_split) <= lds_bytes;
 }
 
 int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, int I) {
