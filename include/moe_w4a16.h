@@ -358,8 +358,11 @@ size_t moe_block_workspace_bytes(int64_t T, int32_t top_k, int32_t E,
  * and moe_combine over E + 1 experts and top_k + 1 slots per token, so the
  * shared expert's rows run in the same launches as the routed experts' rows
  * and its output (weight 1) joins the fp32 sum before the one rounding to
- * fp16.  out is what those calls produce, bit for bit.  Sections as
- * moe_router_gate and moe_route_shared.
+ * fp16.  out is what those calls produce, bit for bit, when the plan keeps
+ * the shared expert in the FFN's kernels (shared_mfma = 0); the default at
+ * GEMV sizes runs its rows on the matrix cores in extra workgroups of the
+ * same launches (shared_mfma = 1), which changes the order of its fp32 sums
+ * only.  Sections as moe_router_gate and moe_route_shared.
  *
  *   x            in   fp16 [T, H]
  *   gate_weight  in   fp16 [E, H]
@@ -409,6 +412,11 @@ typedef struct moe_plan {
                              (the down stage takes at most 4)                         */
   int32_t cost_split;     /* GEMV: 1 share work out by cost (rows per expert), 0 evenly */
   int32_t router_gemv;    /* gate projection: 1 GEMV, 0 matrix cores                  */
+  int32_t shared_mfma;    /* GEMV with a shared expert: 1 its rows on the matrix cores
+                             in extra workgroups of the same launches (T <= 32, with
+                             T x H and 2 T x I fp16 A rows and their K-split partial
+                             sums in one workgroup's LDS: T <= 22 at H = 2560),
+                             0 in the GEMV with the routed experts                    */
 } moe_plan;
 
 /*

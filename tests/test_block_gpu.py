@@ -155,7 +155,8 @@ def test_route_shared_matches_oracle(dev, T, E, k):
 # --------------------------------------------------------------------------- #
 # the whole block
 # --------------------------------------------------------------------------- #
-def _run_block(host, shape, dev, shared=True):
+def _run_block(host, shape, dev, shared=True, plan=None):
+    """The block on poisoned buffers, with the default plan or `plan` (a dict)."""
     from w4a16_group_quantized_amd import ops
 
     w = ops.weights_to_device(host, dev)
@@ -166,7 +167,14 @@ def _run_block(host, shape, dev, shared=True):
     blk.out.fill_(float("nan"))
     blk.logits.fill_(float("nan"))
     torch.cuda.synchronize()
-    out = blk(x, gw, w)
+    if plan is None:
+        out = blk(x, gw, w)
+    else:
+        p = ops.Plan()
+        for key, v in plan.items():
+            setattr(p, key, v)
+        out = ops.moe_block_forward_plan(x, gw, shape.top_k, w, shared, p, blk.ws, blk.logits,
+                                         blk.out)
     torch.cuda.synchronize()
     v = blk.views()
     got = {"out": out.cpu().numpy(), "logits": blk.logits.cpu().numpy(),
@@ -212,6 +220,8 @@ def _block_check(shape, seed, dev, dtype=np.float64):
     (64, 6, 512, 256, 40),      # one-launch router + permutation, matrix-core FFN
     (64, 6, 512, 256, 300),     # router and permutation kernels, matrix-core FFN
     (63, 62, 256, 128, 9),      # top_k + 1 = 63 slots, E + 1 = 64 experts
+    (64, 6, 512, 256, 20),      # shared expert on the matrix cores: a ragged 32-row tile
+    (128, 4, 512, 160, 32),     # and a full one
 ])
 def test_block_matches_oracle(dev, E, k, H, I, T):
     _block_check(_shape(E, k, H, I, T), 7, dev)
@@ -225,12 +235,15 @@ def test_block_prefill_workload_full(dev):
 @pytest.mark.parametrize("T", [2, 8, 40, 300])
 def test_block_matches_its_steps(dev, T):
     """moe_block_forward equals moe_router_gate, moe_route_shared, moe_permute,
-    moe_w4a16_grouped_ffn and moe_combine called one after another, bit for bit."""
+    moe_w4a16_grouped_ffn and moe_combine called one after another, bit for bit,
+    when the shared expert runs in the FFN with the routed experts (the step
+    calls know no shared expert; its matrix-core form is compared below)."""
     from w4a16_group_quantized_amd import ops
 
     shape = _shape(64, 6, 512, 256, T)
     host = synth.make_block_inputs(shape, 8, shared=True)
-    got, (x, gw, w, blk) = _run_block(host, shape, dev)
+    plan = dict(ops.plan_default(T, 6, 64, 512, 256, shared=True).as_dict(), shared_mfma=0)
+    got, (x, gw, w, blk) = _run_block(host, shape, dev, plan=plan)
     logits = ops.moe_router_gate(x, gw)
     ids, wts = ops.moe_route_shared(logits, shape.top_k)
     perm = ops.moe_permute(ids, shape.E + 1)
@@ -241,6 +254,32 @@ def test_block_matches_its_steps(dev, T):
     assert np.array_equal(ids.cpu().numpy(), got["topk_ids"])
     assert np.array_equal(y.cpu().numpy().view(np.int32), got["y_sorted"].view(np.int32))
     assert np.array_equal(out.cpu().numpy().view(np.int16), got["out"].view(np.int16))
+
+
+@pytest.mark.parametrize("E,k,H,I,T", [(512, 10, 2560, 640, 8), (64, 6, 512, 256, 1),
+                                       (64, 6, 512, 160, 32)])
+def test_shared_expert_on_matrix_cores_matches_the_gemv_form(dev, E, k, H, I, T):
+    """The shared expert's rows on the matrix cores (extra workgroups) against
+    the same rows in the GEMV with the routed experts: the routed rows bit for
+    bit, the shared rows within the y_sorted bound (the order of fp32 sums
+    differs), and both outputs within the layer tolerance of the oracle."""
+    from w4a16_group_quantized_amd import ops
+
+    shape = _shape(E, k, H, I, T)
+    host = synth.make_block_inputs(shape, 15, shared=True)
+    base = ops.plan_default(T, k, E, H, I, shared=True).as_dict()
+    assert base["shared_mfma"] == 1
+    mf, _ = _run_block(host, shape, dev, plan=base)
+    gv, _ = _run_block(host, shape, dev, plan=dict(base, shared_mfma=0))
+    S = T * k
+    assert np.array_equal(mf["topk_ids"], gv["topk_ids"])
+    assert np.array_equal(mf["y_sorted"][:S].view(np.int32), gv["y_sorted"][:S].view(np.int32))
+    assert_y_close(mf["y_sorted"][S:], gv["y_sorted"][S:], f"{shape} shared rows, MFMA vs GEMV")
+    ref = oracle.block(host, k, shared=True)
+    bound = _logit_bound(host["x"], host["gate_w"])
+    clear = ~_ambiguous_tokens(ref["logits"], bound, k)
+    assert_fp16_close(mf["out"][clear], ref["out"][clear], f"{shape} MFMA shared")
+    assert_fp16_close(gv["out"][clear], ref["out"][clear], f"{shape} GEMV shared")
 
 
 @pytest.mark.parametrize("T", [8, 300])

@@ -69,10 +69,17 @@ def test_rows_per_pass_and_cost_split():
     assert plan(8)["rows_per_pass"] == 2 and plan(8)["cost_split"] == 0
     assert plan(9)["rows_per_pass"] == 2 and plan(9)["cost_split"] == 0
     assert plan(10)["rows_per_pass"] == 4 and plan(10)["cost_split"] == 1
-    # a shared expert holds all T rows: one pass over them, work shared out by cost
-    assert plan(8, shared=True)["rows_per_pass"] == 8 and plan(8, shared=True)["cost_split"] == 1
-    assert plan(3, shared=True)["rows_per_pass"] == 4 and plan(3, shared=True)["cost_split"] == 1
-    assert plan(2, shared=True)["rows_per_pass"] == 2 and plan(2, shared=True)["cost_split"] == 0
+    # a shared expert with the GEMV runs on the matrix cores in extra workgroups;
+    # the GEMV's rows per pass and split then follow the routed experts
+    assert plan(8, shared=True)["shared_mfma"] == 1 and plan(8, shared=True)["rows_per_pass"] == 2
+    assert plan(16, shared=True)["shared_mfma"] == 1
+    # its A rows (T x H fp16) and the K-split partial sums share one
+    # workgroup's LDS: 22 rows of 2560 fit, 23 do not
+    assert plan(22, shared=True)["shared_mfma"] == 1
+    assert plan(23, shared=True)["shared_mfma"] == 0
+    assert plan(8, H=16384, shared=True)["shared_mfma"] == 0
+    assert plan(33, shared=True)["shared_mfma"] == 0          # matrix-core FFN: in its tile list
+    assert plan(8)["shared_mfma"] == 0
     # the shared expert counts for the one-launch routing limit and the M-tile switch
     assert plan(8, E=1024, shared=True)["route"] == ops.ROUTE_SEPARATE
     assert plan(8, E=1023, shared=True)["route"] == ops.ROUTE_IN_GATE_UP
@@ -112,6 +119,7 @@ def test_layer_rejects_plans_the_sizes_do_not_allow():
     assert _layer(lib, dict(base, route=3)) == ops.MOE_ERR_INVALID_ARG
     assert _layer(lib, dict(base, rows_per_pass=3)) == ops.MOE_ERR_INVALID_ARG
     assert _layer(lib, dict(base, cost_split=2)) == ops.MOE_ERR_INVALID_ARG
+    assert _layer(lib, dict(base, shared_mfma=1)) == ops.MOE_ERR_INVALID_ARG   # no shared expert
     assert _layer(lib, dict(base, ffn=ops.FFN_MFMA)) == ops.MOE_ERR_UNSUPPORTED  # routing in gate/up
     big = plan(65)
     assert _layer(lib, dict(big, ffn=ops.FFN_GEMV), T=65) == ops.MOE_ERR_UNSUPPORTED

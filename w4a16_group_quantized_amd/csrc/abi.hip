@@ -71,6 +71,7 @@ void run_gate_up(GateUpArgs a, const Plan& pl, void* workspace, hipStream_t st) 
   a.lanes = pl.lanes_gate_up;
   a.rows_per_pass = pl.rows_per_pass;
   a.cost_split = pl.cost_split;
+  a.shared_mfma = pl.shared_mfma;
   a.msub = pl.msub;
   if (pl.ffn == MOE_FFN_GEMV) {
     launch_gate_up_decode(a, ws, st);
@@ -86,6 +87,7 @@ void run_down(DownArgs d, const Plan& pl, void* workspace, hipStream_t st) {
   d.lanes = pl.lanes_down;
   d.rows_per_pass = pl.rows_per_pass;
   d.cost_split = pl.cost_split;
+  d.shared_mfma = pl.shared_mfma;
   d.msub = pl.msub;
   if (pl.ffn == MOE_FFN_GEMV)
     launch_down_decode(d, ws, st);
@@ -519,6 +521,7 @@ static int layer_run(const float* logits, const uint16_t* x, int64_t T, int32_t 
     a.lanes = pl.lanes_gate_up;
     a.rows_per_pass = pl.rows_per_pass;
     a.cost_split = pl.cost_split;
+    a.shared_mfma = pl.shared_mfma;
     const RouteOut r{w.ids, w.weights, w.offsets, w.sorted, w.slot_rows, w.active, w.num_active};
     launch_route_gate_up_decode(logits, a, r, fws, st);
   } else {

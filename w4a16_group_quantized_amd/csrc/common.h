@@ -84,6 +84,7 @@ struct GateUpArgs {
   int lanes = 0;          // GEMV: lanes per weight row (from the plan)
   int rows_per_pass = 0;  // GEMV: A rows of an expert per weight pass (from the plan)
   int cost_split = 0;     // GEMV: units shared out by cost (from the plan)
+  int shared_mfma = 0;    // GEMV: the shared expert (the last expert) on the matrix cores
   int msub = 0;           // MFMA: 32-row subtiles per M-tile (from the plan)
   const int* offsets;
   const int* sorted_slots;
@@ -98,6 +99,7 @@ struct DownArgs {
   int lanes = 0;  // as in GateUpArgs
   int rows_per_pass = 0;
   int cost_split = 0;
+  int shared_mfma = 0;
   int msub = 0;
   const int* offsets;
   const int* active;
@@ -131,6 +133,9 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
 // device gives a workgroup cannot run.
 size_t gemv_min_lds(bool gate_up, bool route, int64_t T, int top_k, int E, int H, int I,
                     int lanes, bool cost_split);
+// LDS of the shared expert's matrix-core workgroups inside the GEMV launches
+// (A rows of both stages and the K-split partial sums), T <= 32.
+size_t shared_mfma_lds(int64_t T, int H, int I);
 constexpr size_t kGfx950LdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
 
 // Matrix-core variant: a prep kernel (tile list of M-tiles of msub 32-row
@@ -165,6 +170,52 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
 // Round to nearest even (the default rounding mode of v_cvt_f16_f32).
 __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// ---- matrix-core operands (v_mfma_f32_32x32x16_f16) --------------------------
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+
+// Position of column c once its 8-wide block is permuted to k-slot order
+// (0, 4, 1, 5, 2, 6, 3, 7).
+__device__ __forceinline__ int slot_pos(int c) {
+  return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1);
+}
+
+// 8 consecutive fp16 (4 dwords: (a0,a1) (a2,a3) (a4,a5) (a6,a7)) reordered
+// to the k-slot order (a0,a4) (a1,a5) (a2,a6) (a3,a7).
+__device__ __forceinline__ uint4 permute8(uint4 d) {
+  return make_uint4((d.x & 0xFFFFu) | (d.z << 16), (d.x >> 16) | (d.z & 0xFFFF0000u),
+                    (d.y & 0xFFFFu) | (d.w << 16), (d.y >> 16) | (d.w & 0xFFFF0000u));
+}
+
+// (q - z) of one packed word as 8 fp16 in k-slot order, exactly.  m1024 holds
+// -(1024 + z) and m64 holds -(64 + z) in both halves.
+__device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t bias, h2 m1024, h2 m64) {
+  const uint32_t w8 = w >> 8;
+  const h2 pa = __builtin_bit_cast(h2, (w & 0x000F000Fu) | bias);   // 1024 + q0, 1024 + q4
+  const h2 pb = __builtin_bit_cast(h2, (w & 0x00F000F0u) | bias);   // 1024 + 16 q1, ...
+  const h2 pc = __builtin_bit_cast(h2, (w8 & 0x000F000Fu) | bias);  // 1024 + q2, 1024 + q6
+  const h2 pd = __builtin_bit_cast(h2, (w8 & 0x00F000F0u) | bias);  // 1024 + 16 q3, ...
+  const h2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+  const h2 r0 = pa + m1024;              // q0 - z, q4 - z
+  const h2 r1 = pb * sixteenth + m64;    // q1 - z, q5 - z
+  const h2 r2 = pc + m1024;
+  const h2 r3 = pd * sixteenth + m64;
+  half8 out;
+  out[0] = r0[0]; out[1] = r0[1]; out[2] = r1[0]; out[3] = r1[1];
+  out[4] = r2[0]; out[5] = r2[1]; out[6] = r3[0]; out[7] = r3[1];
+  return out;
+}
+
+
+// The two zero-point terms of dequant_word for zero code zc: -(1024 + z) and
+// -(64 + z) (the latter for the nibbles read 16 times too large), in both
+// halves.
+__device__ __forceinline__ void zero_terms(uint32_t zc, h2& m1024, h2& m64) {
+  m1024 = __builtin_bit_cast(h2, (0xE400u | zc) * 0x00010001u);
+  m64 = __builtin_bit_cast(h2, (0xD400u | (zc << 4)) * 0x00010001u);
 }
 
 }  // namespace moe

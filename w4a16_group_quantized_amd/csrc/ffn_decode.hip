@@ -268,6 +268,11 @@ struct DecodeArgs {
   float* y;                // stage 2 output
   int* cost_out;           // stage 1: per-unit cost prefix [num_active + 1], workgroup 0 writes it
   const int* cost_in;      // stage 2: that prefix
+  // a shared expert (the last expert, E - 1, holding sorted rows [shared_row0,
+  // shared_row0 + T)) on the matrix cores in shared_wgs extra workgroups;
+  // the units then cover the other active experts only
+  int shared_wgs;
+  int shared_row0;
   // stage 1 that routes the tokens itself: logits in; the routing (as
   // moe_route_permute returns it) written out by workgroup 0.  E and top_k
   // count the shared expert when `shared` is 1: the logits then have E - 1
@@ -371,6 +376,182 @@ struct WinExpert {
   int e, r0, rows;
 };
 
+// ---------------------------------------------------------- shared expert --
+// A shared expert holds all T tokens (sorted rows [shared_row0, +T)): a small
+// dense GEMM, which extra workgroups of the launch run on the matrix cores
+// while the others stream the routed experts.  A workgroup takes kShTiles
+// column tiles of 32 weight rows (stage 1: 16 gate columns in lanes j < 16 of
+// each lane half and the matching 16 up columns in lanes j >= 16; stage 2: 32
+// output columns) and splits K over its 16 / kShTiles waves per tile; their
+// partial sums meet in LDS and are added in a fixed order.  A (the T x rows,
+// or the T act rows hi and lo) is staged once in LDS, permuted to the nibble
+// k-slot order; the weight loads run kShDepth groups ahead in a register
+// ring.  Per quantisation group, two v_mfma_f32_32x32x16_f16 (stage 2: four,
+// act hi then lo) with the exact integer B = q - z make a partial that is
+// scaled by the group's scale in fp32, as in the matrix-core FFN.  Rows past T
+// are zero operands; columns past the matrix read zeros.  Lane (h, j) ends
+// with rows 8 (v / 4) + 4 h + v % 4 of column j.
+constexpr int kShDepth = 4;                     // weight groups in flight per lane
+template <bool GATE_UP>
+struct ShCfg {
+  static constexpr int kTiles = GATE_UP ? 4 : 8;           // column tiles per workgroup
+  static constexpr int kSplits = kWaves / kTiles;          // waves per tile, over K
+  static constexpr int kCols = GATE_UP ? 16 : 32;          // new columns per tile
+  static constexpr int kCopies = GATE_UP ? 1 : 2;          // A copies: x, or act hi and lo
+};
+
+// LDS bytes of the shared-expert path: A rows (row stride K + 8 halves, so
+// that the 32 lanes reading one k offset of different rows use different
+// banks) and the partial sums of all splits but the first.
+__host__ __device__ inline size_t shared_lds_bytes(bool gate_up, int T, int K) {
+  const int tiles = gate_up ? ShCfg<true>::kTiles : ShCfg<false>::kTiles;
+  const int copies = gate_up ? 1 : 2;
+  return static_cast<size_t>(copies) * T * (K + 8) * 2 +
+         static_cast<size_t>(tiles) * (kWaves / tiles - 1) * 64 * 16 * 4;
+}
+
+struct ShSlot {
+  uint4 q;
+  uint32_t z, s;
+};
+
+template <bool GATE_UP>
+__device__ __forceinline__ void shared_expert_mfma(const DecodeArgs& p, uint32_t* lds, int wg) {
+  using Cfg = ShCfg<GATE_UP>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, j = lane & 31;
+  const int I = p.I, H = p.H, T = p.T;
+  const int K = GATE_UP ? H : I;
+  const int G = K / kGroup;
+  const int rows_w = GATE_UP ? 2 * I : H;
+  const int stride = K + 8;                                // LDS row stride, halves
+  uint16_t* as = reinterpret_cast<uint16_t*>(lds);
+  float* part = reinterpret_cast<float*>(as + Cfg::kCopies * T * stride);
+
+  // ---- stage A: T rows of K, 16 bytes per thread per step, k-slot order
+  {
+    const int chunks = T * (K / 8);
+    for (int c = static_cast<int>(threadIdx.x); c < Cfg::kCopies * chunks; c += kThreads) {
+      const int cp = c / chunks, cc = c - cp * chunks;
+      const int r = cc / (K / 8), k8 = cc - r * (K / 8);
+      const uint16_t* src = GATE_UP ? p.x + static_cast<size_t>(r) * H
+                                    : (cp ? p.a_lo : p.a_hi) + static_cast<size_t>(p.shared_row0 + r) * I;
+      const uint4 v = reinterpret_cast<const uint4*>(src)[k8];
+      *reinterpret_cast<uint4*>(as + (cp * T + r) * stride + 8 * k8) = permute8(v);
+    }
+  }
+  __syncthreads();
+
+  const int tile = wg * Cfg::kTiles + wave % Cfg::kTiles;
+  const int split = wave / Cfg::kTiles;
+  int n, col;
+  bool live;
+  if (GATE_UP) {
+    col = tile * 16 + (j & 15);
+    live = tile * 16 < I;
+    n = col < I ? (j < 16 ? col : I + col) : rows_w;   // rows_w: no row, zeros
+  } else {
+    col = tile * 32 + j;
+    live = tile * 32 < H;
+    n = col < H ? col : rows_w;
+  }
+  const int g0 = split * ((G + Cfg::kSplits - 1) / Cfg::kSplits);
+  const int g1 = min(G, g0 + (G + Cfg::kSplits - 1) / Cfg::kSplits);
+  const ExpertBufs wb = expert_bufs(p, rows_w, G, p.E - 1);
+  const uint32_t zshift = 4u * static_cast<uint32_t>(n & 7);
+  uint32_t bias;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));
+  float16v acc = {};
+  if (live) {  // uniform: the whole wave
+    ShSlot ring[kShDepth];
+    auto issue = [&](int d, int g) {
+      // past g1 (the ring's tail): a row index past the matrix, zeros
+      const uint32_t row = g < g1 ? static_cast<uint32_t>(n) : static_cast<uint32_t>(rows_w);
+      const uint32_t gg = static_cast<uint32_t>(g < g1 ? g : 0);
+      ring[d].q = load_b128(wb.q, (row * G + gg) * 16u);
+      ring[d].z = __builtin_amdgcn_raw_buffer_load_b32(
+          wb.z, static_cast<int>(((row >> 3) * G + gg) * 4u), 0, 0);
+      ring[d].s = __builtin_amdgcn_raw_buffer_load_b16(
+          wb.s, static_cast<int>((row * G + gg) * 2u), 0, 0);
+    };
+#pragma unroll
+    for (int d = 0; d < kShDepth; ++d) issue(d, g0 + d);
+    const half8 zero8 = {};
+    for (int g = g0; g < g1; g += kShDepth) {
+#pragma unroll
+      for (int d = 0; d < kShDepth; ++d) {
+        const int gd = g + d;
+        if (gd < g1) {
+          auto a_op = [&](int cp, int t) -> half8 {
+            if (j >= T) return zero8;
+            return *reinterpret_cast<const half8*>(as + (cp * T + j) * stride + 32 * gd + 16 * t + 8 * h);
+          };
+          const half8 a0 = a_op(0, 0), a1 = a_op(0, 1);
+          const ShSlot sl = ring[d];
+          h2 m1024, m64;
+          zero_terms((sl.z >> zshift) & 0xFu, m1024, m64);
+          // MFMA t takes k [16 t + 8 h, +8) of the group: word 2 t + h of the codes
+          const half8 b0 = dequant_word(h ? sl.q.y : sl.q.x, bias, m1024, m64);
+          const half8 b1 = dequant_word(h ? sl.q.w : sl.q.z, bias, m1024, m64);
+          float16v pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, float16v{}, 0, 0, 0);
+          pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, pr, 0, 0, 0);
+          if (!GATE_UP) {
+            const half8 l0 = a_op(1, 0), l1 = a_op(1, 1);
+            pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(l0, b0, pr, 0, 0, 0);
+            pr = __builtin_amdgcn_mfma_f32_32x32x16_f16(l1, b1, pr, 0, 0, 0);
+          }
+          const float sc = half_bits_to_float(static_cast<uint16_t>(sl.s));
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[v] = fmaf(sc, pr[v], acc[v]);
+          issue(d, gd + kShDepth);  // refill the slot (a no-load past the end)
+        }
+      }
+    }
+  }
+  // splits 1.. hand their partial sums to split 0 of their tile
+  if (split > 0) {
+    float* dst = part + ((wave % Cfg::kTiles) * (Cfg::kSplits - 1) + split - 1) * 64 * 16;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dst[v * 64 + lane] = acc[v];
+  }
+  __syncthreads();
+  if (split > 0 || !live) return;
+  for (int sp = 1; sp < Cfg::kSplits; ++sp) {
+    const float* src = part + ((wave % Cfg::kTiles) * (Cfg::kSplits - 1) + sp - 1) * 64 * 16;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] += src[v * 64 + lane];
+  }
+  if (GATE_UP) {
+    // lanes j < 16 hold gate and lanes j + 16 the up value of the same
+    // column; each lane of the pair finishes 8 of the 16 rows
+    const bool low = j < 16;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float send = low ? acc[u + 8] : acc[u];
+      const float recv = __shfl_xor(send, 16, 64);
+      const int v = low ? u : u + 8;
+      const float gate = low ? acc[u] : recv;
+      const float up = low ? recv : acc[u + 8];
+      const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+      if (r < T && col < I) {
+        const float act = gate / (1.f + expf(-gate)) * up;
+        const uint16_t hi = float_to_half_bits(act);
+        const uint16_t lo = float_to_half_bits(act - half_bits_to_float(hi));
+        const size_t idx = static_cast<size_t>(p.shared_row0 + r) * I + col;
+        p.act_hi[idx] = hi;
+        p.act_lo[idx] = lo;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+      if (r < T && col < H) p.y[static_cast<size_t>(p.shared_row0 + r) * H + col] = acc[v];
+    }
+  }
+}
+
 // NPL > 0 (stage 1 only): the workgroup first routes the tokens itself, with
 // the router's and permutation's own steps (route.h, permute.h), from
 // logits of E <= 64 NPL experts; workgroup 0 writes the routing out.  Every
@@ -391,6 +572,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   // the wave index is the same in every lane; saying so keeps the unit
   // bookkeeping in scalar registers and its branches uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (static_cast<int>(blockIdx.x) >= geo.nwg) {  // the extra workgroups: the shared expert
+    shared_expert_mfma<GATE_UP>(p, lds, static_cast<int>(blockIdx.x) - geo.nwg);
+    return;
+  }
   const int k = lane / C, lc = lane & (C - 1);
   uint32_t* frags = lds;
   uint16_t* scales = reinterpret_cast<uint16_t*>(lds + kXE * NF * G * kFragDwords);
@@ -460,6 +645,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   } else {
     n_active = *p.num_active;
   }
+  // the shared expert is the last active expert; its extra workgroups take it
+  if (p.shared_wgs > 0) n_active -= 1;
   auto active_at = [&](int a) { if constexpr (NPL > 0) return ract[a]; else return p.active[a]; };
   auto offset_at = [&](int e) { if constexpr (NPL > 0) return roff[e]; else return p.offsets[e]; };
   auto sorted_at = [&](int r) { if constexpr (NPL > 0) return rsorted[r]; else return p.sorted_slots[r]; };
@@ -749,7 +936,7 @@ int cost_table_ints(int slots) { return (slots + 1 + kScanThreads / 64 + 1 + 3) 
 
 template <bool GATE_UP, int NPL>
 void launch_decode_npl(const DecodeArgs& p, Geom geo, int na, size_t lds, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(geo.nwg)), block(kThreads);
+  const dim3 grid(static_cast<unsigned>(geo.nwg + p.shared_wgs)), block(kThreads);
   if constexpr (GATE_UP) {
     if (na == 8) {
       hipLaunchKernelGGL((decode_kernel<GATE_UP, 8, NPL>), grid, block, lds, stream, p, geo);
@@ -770,13 +957,15 @@ void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream,
                    int rows_per_pass, int cost_split) {
   // (p.E is set by every caller: the share arithmetic's width depends on it)
   const DeviceInfo dev = device_info();
-  geo.nwg = dev.cus;
+  geo.nwg = dev.cus - p.shared_wgs;  // with the shared expert's workgroups, one per compute unit
   geo.weighted = cost_split && slots <= kThreads;  // the cost scan: one expert per thread
   geo.ucap = geo.weighted ? cost_table_ints(slots) : 0;
   const size_t rbytes = route ? route_lds_bytes(p.E, p.T * p.top_k) : 0;
   const int na =
       plan<GATE_UP>(geo, slots, dev, rbytes + static_cast<size_t>(geo.ucap) * 4, rows_per_pass);
-  const size_t lds = launch_lds<GATE_UP>(geo, na) + rbytes;  // the cost table included
+  size_t lds = launch_lds<GATE_UP>(geo, na) + rbytes;  // the cost table included
+  if (p.shared_wgs > 0)
+    lds = std::max(lds, shared_lds_bytes(GATE_UP, p.T, GATE_UP ? p.H : p.I));
   if constexpr (GATE_UP) {
     if (route) {
       const int El = p.E - p.shared;  // logits per token
@@ -788,6 +977,21 @@ void launch_decode(const DecodeArgs& p, Geom geo, int slots, hipStream_t stream,
     }
   }
   launch_decode_npl<GATE_UP, 0>(p, geo, na, lds, stream);
+}
+
+// The shared expert (the last expert, holding the last T sorted rows) on the
+// matrix cores: column tiles of 16 gate columns (stage 1) or 32 output
+// columns (stage 2), ShCfg::kTiles of them per extra workgroup.
+template <bool GATE_UP>
+void set_shared(DecodeArgs& p, int shared_mfma, int T, int top_k, int I, int H) {
+  if (!shared_mfma) {
+    p.shared_wgs = 0;
+    p.shared_row0 = 0;
+    return;
+  }
+  const int tiles = GATE_UP ? (I + 15) / 16 : (H + 31) / 32;
+  p.shared_wgs = (tiles + ShCfg<GATE_UP>::kTiles - 1) / ShCfg<GATE_UP>::kTiles;
+  p.shared_row0 = T * (top_k - 1);
 }
 
 }  // namespace
@@ -806,6 +1010,13 @@ size_t gemv_min_lds(bool gate_up, bool route, int64_t T, int top_k, int E, int H
   if (route) need += route_lds_bytes(E, static_cast<int>(T * top_k));
   if (cost_split && slots <= kThreads) need += static_cast<size_t>(cost_table_ints(slots)) * 4;
   return need;
+}
+
+// LDS the shared expert's matrix-core workgroups take at T tokens: the larger
+// of the two stages.
+size_t shared_mfma_lds(int64_t T, int H, int I) {
+  const int t = static_cast<int>(std::min<int64_t>(T, 32));
+  return std::max(shared_lds_bytes(true, t, H), shared_lds_bytes(false, t, I));
 }
 
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
@@ -832,6 +1043,7 @@ void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStrea
   p.act_hi = ws.act_hi;
   p.act_lo = ws.act_lo;
   p.cost_out = ws.tiles;  // the tile list region is free at decode sizes
+  set_shared<true>(p, a.shared_mfma, a.T, a.top_k, a.I, a.H);
   launch_decode<true>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_per_pass, a.cost_split);
 }
 
@@ -855,6 +1067,7 @@ void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const
   p.act_hi = ws.act_hi;
   p.act_lo = ws.act_lo;
   p.cost_out = ws.tiles;
+  set_shared<true>(p, a.shared_mfma, a.T, a.top_k, a.I, a.H);
   p.logits = logits;
   p.E = a.E;
   p.shared = a.shared;
@@ -890,6 +1103,7 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
   p.E = a.E;
   p.y = a.y;
   p.cost_in = ws.tiles;  // written by the gate/up kernel
+  set_shared<false>(p, a.shared_mfma, a.T, a.top_k, a.I, a.H);
   launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_per_pass, a.cost_split);
 }
 

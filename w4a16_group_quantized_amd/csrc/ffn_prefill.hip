@@ -45,9 +45,6 @@
 namespace moe {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int kSub = 32;                   // MFMA tile edge
 constexpr int kWaves = 4;
@@ -89,38 +86,6 @@ struct PrefillArgs {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
                                            kBufferFlags);
-}
-
-// Position of column c once its 8-wide block is permuted to k-slot order
-// (0, 4, 1, 5, 2, 6, 3, 7).
-__device__ __forceinline__ int slot_pos(int c) {
-  return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1);
-}
-
-// 8 consecutive fp16 (4 dwords: (a0,a1) (a2,a3) (a4,a5) (a6,a7)) reordered
-// to the k-slot order (a0,a4) (a1,a5) (a2,a6) (a3,a7).
-__device__ __forceinline__ uint4 permute8(uint4 d) {
-  return make_uint4((d.x & 0xFFFFu) | (d.z << 16), (d.x >> 16) | (d.z & 0xFFFF0000u),
-                    (d.y & 0xFFFFu) | (d.w << 16), (d.y >> 16) | (d.w & 0xFFFF0000u));
-}
-
-// (q - z) of one packed word as 8 fp16 in k-slot order, exactly.  m1024 holds
-// -(1024 + z) and m64 holds -(64 + z) in both halves.
-__device__ __forceinline__ half8 dequant_word(uint32_t w, uint32_t bias, h2 m1024, h2 m64) {
-  const uint32_t w8 = w >> 8;
-  const h2 pa = __builtin_bit_cast(h2, (w & 0x000F000Fu) | bias);   // 1024 + q0, 1024 + q4
-  const h2 pb = __builtin_bit_cast(h2, (w & 0x00F000F0u) | bias);   // 1024 + 16 q1, ...
-  const h2 pc = __builtin_bit_cast(h2, (w8 & 0x000F000Fu) | bias);  // 1024 + q2, 1024 + q6
-  const h2 pd = __builtin_bit_cast(h2, (w8 & 0x00F000F0u) | bias);  // 1024 + 16 q3, ...
-  const h2 sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-  const h2 r0 = pa + m1024;              // q0 - z, q4 - z
-  const h2 r1 = pb * sixteenth + m64;    // q1 - z, q5 - z
-  const h2 r2 = pc + m1024;
-  const h2 r3 = pd * sixteenth + m64;
-  half8 out;
-  out[0] = r0[0]; out[1] = r0[1]; out[2] = r1[0]; out[3] = r1[1];
-  out[4] = r2[0]; out[5] = r2[1]; out[6] = r3[0]; out[7] = r3[1];
-  return out;
 }
 
 // Per-lane weight operands of one stage: codes of kKC / 2 group pairs (lane

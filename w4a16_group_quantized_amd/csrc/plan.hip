@@ -74,20 +74,17 @@ Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
   p.msub = S >= kMsub4RowsPerExpert * static_cast<int64_t>(EP) ? 4 : 1;
   p.lanes_gate_up = gemv_lanes(H / kGroup);
   p.lanes_down = gemv_lanes(I / kGroup);
-  // A shared expert holds all T rows: take them (up to 8) in one pass and
-  // share the work out by cost.
-  if (shared) {
-    p.rows_per_pass = pow2_rows(T);
-    p.cost_split = T > 2;
-  } else {
-    p.rows_per_pass = T >= kRows4MinT ? 4 : (T >= 2 ? 2 : 1);
-    p.cost_split = T >= kRows4MinT;
-  }
+  // A shared expert with the GEMV runs on the matrix cores in extra
+  // workgroups; the GEMV then holds the routed experts only.
+  p.shared_mfma = shared && p.ffn == MOE_FFN_GEMV && shared_mfma_lds(T, H, I) <= kGfx950LdsBytes;
+  p.rows_per_pass = T >= kRows4MinT ? 4 : (T >= 2 ? 2 : 1);
+  p.cost_split = T >= kRows4MinT;
   p.router_gemv = T <= kRouterGemvMaxT && T * static_cast<int64_t>(H) * 2 <= kRouterGemvMaxXBytes;
   // the GEMV's A fragments of a long K (I near 16384 for the down stage)
   // do not fit a workgroup's LDS: the matrix cores then take every size
   if (p.ffn == MOE_FFN_GEMV && !gemv_fits(p, T, top_k, E, shared, H, I, kGfx950LdsBytes)) {
     p.ffn = MOE_FFN_MFMA;
+    p.shared_mfma = 0;
     if (p.route == MOE_ROUTE_IN_GATE_UP)
       p.route = T <= kRouteOneLaunchMaxT && EP <= kRouteOneLaunchMaxE ? MOE_ROUTE_ONE_LAUNCH
                                                                       : MOE_ROUTE_SEPARATE;
@@ -117,6 +114,13 @@ int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, in
   if (!lanes_ok(p.lanes_gate_up, H / kGroup) || !lanes_ok(p.lanes_down, I / kGroup))
     return MOE_ERR_INVALID_ARG;
   if (p.router_gemv != 0 && p.router_gemv != 1) return MOE_ERR_INVALID_ARG;
+  if (p.shared_mfma != 0 && p.shared_mfma != 1) return MOE_ERR_INVALID_ARG;
+  if (p.shared_mfma && !shared) return MOE_ERR_INVALID_ARG;
+  // the shared expert's matrix-core workgroups: with the GEMV, up to 32 rows
+  // (one MFMA tile) whose A rows fit in LDS
+  if (p.shared_mfma &&
+      (p.ffn != MOE_FFN_GEMV || T > 32 || shared_mfma_lds(T, H, I) > kGfx950LdsBytes))
+    return MOE_ERR_UNSUPPORTED;
   // what each variant supports (the table above picks within these limits)
   if (p.ffn == MOE_FFN_GEMV && T > kPermBlockTokens) return MOE_ERR_UNSUPPORTED;
   if (p.route == MOE_ROUTE_IN_GATE_UP &&
