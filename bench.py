@@ -87,6 +87,9 @@ def parse_args(argv=None):
     p.add_argument("--sweep-tokens", default=None,
                    help="comma-separated token counts for --sweep instead of "
                         "1,2,4,8,9,16,32,64,128,1024,4096")
+    p.add_argument("--block-only", action="store_true",
+                   help="time only the block (gate projection + routed + shared expert) at the "
+                        "workload and print its object; for kernel traces of the block alone")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB a few times (counter calibration)")
     return p.parse_args(argv)
@@ -874,6 +877,9 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     ops.load_library()
     log(f"workload {args.workload}: {shape} on {torch.cuda.get_device_name(dev)}")
+    if args.block_only:
+        print(json.dumps({"workload": args.workload, "block": measure_block(args, shape, dev)}), flush=True)
+        return 0
 
     host = synth.make_inputs(shape, args.seed)
     m = measure_layer(args, shape, args.workload, host, dev,
