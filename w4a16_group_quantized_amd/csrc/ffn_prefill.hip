@@ -264,7 +264,10 @@ __device__ __forceinline__ void compute_stage(uint32_t tid, const uint16_t* stag
       const h2 m64 = __builtin_bit_cast(h2, (0xD400u | (zc << 4)) * 0x00010001u);
       const half8 b0 = dequant_word(words[gi][0], bias, m1024, m64);
       const half8 b1 = dequant_word(words[gi][1], bias, m1024, m64);
-      const float sf = half_bits_to_float(static_cast<uint16_t>(b.scale(g)));
+      float sf = half_bits_to_float(static_cast<uint16_t>(b.scale(g)));
+      // converted once here: left foldable, every scaling FMA below becomes a
+      // v_fma_mix_f32 (fp16 operand), which issues slower than v_fma_f32
+      asm volatile("" : "+v"(sf));
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const uint16_t* blk = stage + ((g * MSUB + i) * 2) * kBlockHalfs;
