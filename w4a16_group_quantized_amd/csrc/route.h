@@ -113,7 +113,15 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
   for (int j = 0; j < top_k; ++j) {
     const uint32_t hi = static_cast<uint32_t>(key[0] >> 32), lo = static_cast<uint32_t>(key[0]);
     const uint32_t mhi = wave_max_u32(hi);
-    const uint32_t mlo = wave_max_u32(hi == mhi ? lo : 0u);
+    // lanes holding the largest value: almost always one, whose index word
+    // is then read directly; equal values take the maximum of the index
+    // words among them (the lowest expert)
+    const uint64_t cand = __ballot(hi == mhi);
+    uint32_t mlo;
+    if (__popcll(cand) == 1)
+      mlo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), __ffsll(static_cast<long long>(cand)) - 1));
+    else
+      mlo = wave_max_u32(hi == mhi ? lo : 0u);
     const uint64_t best = (static_cast<uint64_t>(mhi) << 32) | mlo;
     // the winning lane drops its first key (written with masks: as selects the
     // compiler turns the shift into an indexed pick over all slots)
