@@ -74,3 +74,13 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr or "single" in res.stderr
+
+
+def test_option_defaults_and_block_only():
+    """No flags: one GPU, the decode workload, the block and prefill objects
+    on; --block-only is accepted and leaves the rest at its defaults."""
+    a = bench.parse_args([])
+    assert a.gpus == 1 and a.workload == bench.DEFAULT_WORKLOAD
+    assert not a.block_only and not a.no_block and not a.no_prefill
+    b = bench.parse_args(["--block-only", "--steps", "8"])
+    assert b.block_only and b.steps == 8 and b.workload == bench.DEFAULT_WORKLOAD
