@@ -112,10 +112,12 @@ DeviceInfo device_info() {
           hipSuccess ||
       cus < 1)
     cus = 256;
+  // without a device to ask (host-side checks on a machine with no GPU), the
+  // gfx950 value the library is built for
   if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev < 0 ? 0 : dev) !=
           hipSuccess ||
-      lds < 65536)
-    lds = 65536;
+      lds < 1)
+    lds = static_cast<int>(kGfx950LdsBytes);
   if (dev >= 0)
     cache[dev].store((static_cast<uint64_t>(cus) << 32) | static_cast<uint32_t>(lds),
                      std::memory_order_relaxed);

@@ -137,6 +137,9 @@ size_t gemv_min_lds(bool gate_up, bool route, int64_t T, int top_k, int E, int H
 // (A rows of both stages and the K-split partial sums), T <= 32.
 size_t shared_mfma_lds(int64_t T, int H, int I);
 constexpr size_t kGfx950LdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+// LDS a decode launch keeps beside its dynamic LDS (the kernels' static LDS,
+// rounded up): every dynamic-size check leaves it free.
+constexpr size_t kDecodeStaticLds = 256;
 
 // Matrix-core variant: a prep kernel (tile list of M-tiles of msub 32-row
 // subtiles built from the routing, x permuted to k-slot order, both into the

@@ -379,10 +379,11 @@ struct WinExpert {
 // ---------------------------------------------------------- shared expert --
 // A shared expert holds all T tokens (sorted rows [shared_row0, +T)): a small
 // dense GEMM, which extra workgroups of the launch run on the matrix cores
-// while the others stream the routed experts.  A workgroup takes kShTiles
-// column tiles of 32 weight rows (stage 1: 16 gate columns in lanes j < 16 of
-// each lane half and the matching 16 up columns in lanes j >= 16; stage 2: 32
-// output columns) and splits K over its 16 / kShTiles waves per tile; their
+// while the others stream the routed experts.  A workgroup takes
+// ShCfg::kTiles column tiles of 32 weight rows (stage 1: 16 gate columns in
+// lanes j < 16 of each lane half and the matching 16 up columns in lanes
+// j >= 16; stage 2: 32 output columns) and splits K over its
+// 16 / ShCfg::kTiles waves per tile; their
 // partial sums meet in LDS and are added in a fixed order.  A (the T x rows,
 // or the T act rows hi and lo) is staged once in LDS, permuted to the nibble
 // k-slot order; the weight loads run kShDepth groups ahead in a register
@@ -396,7 +397,6 @@ template <bool GATE_UP>
 struct ShCfg {
   static constexpr int kTiles = GATE_UP ? 4 : 8;           // column tiles per workgroup
   static constexpr int kSplits = kWaves / kTiles;          // waves per tile, over K
-  static constexpr int kCols = GATE_UP ? 16 : 32;          // new columns per tile
   static constexpr int kCopies = GATE_UP ? 1 : 2;          // A copies: x, or act hi and lo
 };
 
@@ -908,7 +908,7 @@ size_t frag_bytes(const Geom& geo, int na) {
 // workgroup's whole share of units, which is at most ceil(slots * nb / nwg).
 template <bool GATE_UP>
 int plan(Geom& geo, int slots, const DeviceInfo& dev, size_t reserved, int rows_per_pass) {
-  const size_t budget = static_cast<size_t>(dev.lds) - 256 - reserved;
+  const size_t budget = static_cast<size_t>(dev.lds) - kDecodeStaticLds - reserved;
   const size_t unit = static_cast<size_t>(unit_scale_halves(geo.spb)) * 2;
   const int want = static_cast<int>((static_cast<int64_t>(slots) * geo.nb + geo.nwg - 1) / geo.nwg) + 1;
   // the plan's rows per pass; stage 2 stops at 4 (eight rows of hi and lo
@@ -1006,7 +1006,7 @@ size_t gemv_min_lds(bool gate_up, bool route, int64_t T, int top_k, int E, int H
   geo.spb = geo.G / geo.C;
   const int slots = static_cast<int>(std::min<int64_t>(E, T * top_k));
   const size_t frags = gate_up ? frag_bytes<true>(geo, 1) : frag_bytes<false>(geo, 1);
-  size_t need = frags + static_cast<size_t>(unit_scale_halves(geo.spb)) * 2 + 256;
+  size_t need = frags + static_cast<size_t>(unit_scale_halves(geo.spb)) * 2 + kDecodeStaticLds;
   if (route) need += route_lds_bytes(E, static_cast<int>(T * top_k));
   if (cost_split && slots <= kThreads) need += static_cast<size_t>(cost_table_ints(slots)) * 4;
   return need;

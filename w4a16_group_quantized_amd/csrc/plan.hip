@@ -76,7 +76,8 @@ Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
   p.lanes_down = gemv_lanes(I / kGroup);
   // A shared expert with the GEMV runs on the matrix cores in extra
   // workgroups; the GEMV then holds the routed experts only.
-  p.shared_mfma = shared && p.ffn == MOE_FFN_GEMV && shared_mfma_lds(T, H, I) <= kGfx950LdsBytes;
+  p.shared_mfma = shared && p.ffn == MOE_FFN_GEMV &&
+                  shared_mfma_lds(T, H, I) + kDecodeStaticLds <= kGfx950LdsBytes;
   p.rows_per_pass = T >= kRows4MinT ? 4 : (T >= 2 ? 2 : 1);
   p.cost_split = T >= kRows4MinT;
   p.router_gemv = T <= kRouterGemvMaxT && T * static_cast<int64_t>(H) * 2 <= kRouterGemvMaxXBytes;
@@ -96,6 +97,7 @@ bool gemv_fits(const Plan& p, int64_t T, int top_k, int E, int shared, int H, in
                size_t lds_bytes) {
   const int kk = top_k + shared, EP = E + shared;
   const bool route = p.route == MOE_ROUTE_IN_GATE_UP;
+  if (p.shared_mfma && shared_mfma_lds(T, H, I) + kDecodeStaticLds > lds_bytes) return false;
   return gemv_min_lds(true, route, T, kk, EP, H, I, p.lanes_gate_up, p.cost_split) <= lds_bytes &&
          gemv_min_lds(false, false, T, kk, EP, H, I, p.lanes_down, p.cost_split) <= lds_bytes;
 }
@@ -119,7 +121,8 @@ int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, in
   // the shared expert's matrix-core workgroups: with the GEMV, up to 32 rows
   // (one MFMA tile) whose A rows fit in LDS
   if (p.shared_mfma &&
-      (p.ffn != MOE_FFN_GEMV || T > 32 || shared_mfma_lds(T, H, I) > kGfx950LdsBytes))
+      (p.ffn != MOE_FFN_GEMV || T > 32 ||
+       shared_mfma_lds(T, H, I) + kDecodeStaticLds > kGfx950LdsBytes))
     return MOE_ERR_UNSUPPORTED;
   // what each variant supports (the table above picks within these limits)
   if (p.ffn == MOE_FFN_GEMV && T > kPermBlockTokens) return MOE_ERR_UNSUPPORTED;
