@@ -257,7 +257,8 @@ def test_block_matches_its_steps(dev, T):
 
 
 @pytest.mark.parametrize("E,k,H,I,T", [(512, 10, 2560, 640, 8), (64, 6, 512, 256, 1),
-                                       (64, 6, 512, 160, 32)])
+                                       (64, 6, 512, 160, 32),
+                                       (512, 10, 2560, 640, 22)])   # the most LDS it takes
 def test_shared_expert_on_matrix_cores_matches_the_gemv_form(dev, E, k, H, I, T):
     """The shared expert's rows on the matrix cores (extra workgroups) against
     the same rows in the GEMV with the routed experts: the routed rows bit for
