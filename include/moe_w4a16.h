@@ -360,9 +360,9 @@ size_t moe_block_workspace_bytes(int64_t T, int32_t top_k, int32_t E,
  * and its output (weight 1) joins the fp32 sum before the one rounding to
  * fp16.  out is what those calls produce, bit for bit, when the plan keeps
  * the shared expert in the FFN's kernels (shared_mfma = 0); the default at
- * GEMV sizes runs its rows on the matrix cores in extra workgroups of the
- * same launches (shared_mfma = 1), which changes the order of its fp32 sums
- * only.  Sections as moe_router_gate and moe_route_shared.
+ * GEMV sizes from 3 tokens runs its rows on the matrix cores in extra
+ * workgroups of the same launches (shared_mfma = 1), which changes the order
+ * of its fp32 sums only.  Sections as moe_router_gate and moe_route_shared.
  *
  *   x            in   fp16 [T, H]
  *   gate_weight  in   fp16 [E, H]

@@ -72,6 +72,9 @@ def test_rows_per_pass_and_cost_split():
     # a shared expert with the GEMV runs on the matrix cores in extra workgroups;
     # the GEMV's rows per pass and split then follow the routed experts
     assert plan(8, shared=True)["shared_mfma"] == 1 and plan(8, shared=True)["rows_per_pass"] == 2
+    # from 3 tokens: with fewer the shared expert is one more expert of the GEMV
+    assert plan(2, shared=True)["shared_mfma"] == 0 and plan(1, shared=True)["shared_mfma"] == 0
+    assert plan(3, shared=True)["shared_mfma"] == 1
     assert plan(16, shared=True)["shared_mfma"] == 1
     # its A rows (T x H fp16) and the K-split partial sums share one
     # workgroup's LDS: 22 rows of 2560 fit, 23 do not

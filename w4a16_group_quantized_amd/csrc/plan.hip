@@ -41,6 +41,12 @@ constexpr int64_t kMsub4RowsPerExpert = 64;
 // LDS (block at 8 tokens, I = 640: 78.6 us with it, 94.4 us with MFMA).
 constexpr int64_t kRouterGemvMaxT = 16;
 constexpr int64_t kRouterGemvMaxXBytes = 80 * 1024;
+// Shared expert on the matrix cores in extra workgroups of the GEMV launches
+// from 3 tokens; below, as one more expert of the GEMV (block, graph of 16
+// steps, us, matrix cores / GEMV): I = 640: 1 token 52.5 / 35.8, 2: 56.5 /
+// 47.0, 3: 59.5 / 67.6, 4: 64.8 / 85.4, 16: 130.7 / 160.7; I = 160: 1 token
+// 41.1 / 31.9, 2: 46.0 / 35.5, 3: 49.4 / 50.7.
+constexpr int64_t kSharedMfmaMinT = 3;
 
 // Lanes per weight row of a GEMV over K = 32 G: the largest power of two
 // <= 8 that divides G (a lane takes every lanes-th group of the row).
@@ -75,8 +81,9 @@ Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
   p.lanes_gate_up = gemv_lanes(H / kGroup);
   p.lanes_down = gemv_lanes(I / kGroup);
   // A shared expert with the GEMV runs on the matrix cores in extra
-  // workgroups; the GEMV then holds the routed experts only.
-  p.shared_mfma = shared && p.ffn == MOE_FFN_GEMV &&
+  // workgroups (the GEMV then holds the routed experts only) from 3 tokens,
+  // where its A rows fit in LDS.
+  p.shared_mfma = shared && p.ffn == MOE_FFN_GEMV && T >= kSharedMfmaMinT &&
                   shared_mfma_lds(T, H, I) + kDecodeStaticLds <= kGfx950LdsBytes;
   p.rows_per_pass = T >= kRows4MinT ? 4 : (T >= 2 ? 2 : 1);
   p.cost_split = T >= kRows4MinT;
