@@ -438,7 +438,7 @@ int moe_plan_default(int64_t T, int32_t top_k, int32_t E, int32_t shared, int32_
  * GEMV and
  * routing in gate/up or in one launch need T <= 64; routing in gate/up needs
  * the GEMV and E (with the shared expert) <= 1024, and so does the one-launch
- * router; the projection GEMV needs T <= 16 and T * H * 2 <= 80 KiB.
+ * router; the projection GEMV needs T <= 16.
  * MOE_ERR_INVALID_ARG for a malformed plan, MOE_ERR_UNSUPPORTED for one these
  * sizes do not allow; nothing is enqueued then.
  */

@@ -122,6 +122,22 @@ def test_router_gate_matches_oracle(dev, T, E, H):
     _assert_logits(out.cpu().numpy(), exact, _logit_bound(x, gw), f"T={T} E={E} H={H}")
 
 
+@pytest.mark.parametrize("T,H", [(16, 8192), (11, 4096)])   # x 256 KiB, 88 KiB
+def test_router_gemv_beyond_the_default_x_size(dev, T, H):
+    """The projection GEMV takes any H up to 16 tokens (x is read from global
+    memory, not staged): forced by an explicit plan where the default picks
+    the matrix cores (x over 80 KiB), against the oracle's logits."""
+    from w4a16_group_quantized_amd import ops
+
+    shape = _shape(64, 4, H, 64, T)
+    host = synth.make_block_inputs(shape, 11, shared=True)
+    base = ops.plan_default(T, 4, 64, H, 64, shared=True).as_dict()
+    assert base["router_gemv"] == 0
+    got, _ = _run_block(host, shape, dev, plan=dict(base, router_gemv=1))
+    exact = oracle.router_logits(host["x"], host["gate_w"])
+    _assert_logits(got["logits"], exact, _logit_bound(host["x"], host["gate_w"]), f"T={T} H={H} GEMV")
+
+
 def test_router_gate_repeat_is_bitwise_identical(dev):
     from w4a16_group_quantized_amd import ops
 

@@ -8,8 +8,8 @@
 //
 // Few tokens (T <= 16, decode): the work is reading Wg once (2.6 MB at
 // 512 x 2560), so it is a GEMV bound by HBM.  One wave per expert row: lane l
-// takes the row's 16-byte chunks l, l + 64, ..., all issued before x is
-// staged; x (T rows) sits in LDS; v_dot2_f32_f16 multiplies fp16 pairs
+// takes the row's 16-byte chunks l, l + 64, ... and the same chunks of every
+// token's x row (x stays in L2); v_dot2_f32_f16 multiplies fp16 pairs
 // exactly and accumulates in fp32; the 64 lanes' sums are added by DPP and
 // two shuffles in a fixed order.
 //
@@ -20,6 +20,8 @@
 // token-tile-major and every XCD takes a contiguous run of them, so the
 // workgroups of one XCD share each token tile in their L2 (Wg, 2.6 MB, stays
 // in every XCD's L2).
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -30,8 +32,8 @@ typedef float float16v __attribute__((ext_vector_type(16)));
 
 constexpr int kBufferFlags = 0x00020000;  // buffer descriptor word 3 for raw dword access on gfx9
 constexpr int kGemvMaxT = 16;             // tokens of the GEMV variant
-constexpr int kGemvWaves = 4;             // expert rows per workgroup
-constexpr int kGemvWin = 8;               // 16-byte weight loads in flight per lane
+constexpr int kGemvWin = 4;               // 16-byte weight chunks per lane and window
+constexpr int kGemvHalf = kGemvMaxT / 2;  // tokens whose x loads go out together
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -69,53 +71,58 @@ __device__ __forceinline__ float dot8(const uint4 a, const uint4 b, float c) {
 }
 
 // ---- few tokens: one wave per expert row -------------------------------------
-__global__ __launch_bounds__(64 * kGemvWaves) void router_gemv_kernel(
-    const uint16_t* __restrict__ x, int T, int H, const uint16_t* __restrict__ wg, int E,
-    float* __restrict__ logits) {
-  extern __shared__ __align__(16) uint4 xs[];  // [T, H / 8] chunks of x
+// A workgroup of one wave per expert row (E workgroups: every compute unit
+// takes some).  Lane l takes the row's 16-byte chunks l, l + 64, ... in
+// windows of kGemvWin; for each chunk it loads the matching chunk of every
+// token's x row straight from global memory (x, T x H fp16, is read by every
+// row and stays in L2), so nothing waits on a staging pass or a barrier.
+__global__ __launch_bounds__(64) void router_gemv_kernel(const uint16_t* __restrict__ x, int T,
+                                                         int H, const uint16_t* __restrict__ wg,
+                                                         int E, float* __restrict__ logits) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nch = H / 8;                       // 16-byte chunks per row
-  const int per_lane = (nch + 63) / 64;
-  const int e = blockIdx.x * kGemvWaves + wave;
-  // a row past E gets an empty descriptor: its loads return zeros
-  const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(wg + static_cast<size_t>(e < E ? e : 0) * H, e < E ? static_cast<uint32_t>(H) * 2u : 0u);
-
-  uint4 w[kGemvWin];
-  auto load_window = [&](int base) {
-#pragma unroll
-    for (int i = 0; i < kGemvWin; ++i) {
-      const int c = (base + i) * 64 + lane;  // past the row: zeros
-      w[i] = load_b128(rw, static_cast<uint32_t>(c < nch ? c : nch) * 16u);
-    }
-  };
-  load_window(0);
-  // stage x while the first weight loads are in flight
-  const uint4* x4 = reinterpret_cast<const uint4*>(x);
-  for (int i = threadIdx.x; i < T * nch; i += 64 * kGemvWaves) xs[i] = x4[i];
-  __syncthreads();
+  const int e = blockIdx.x;
+  const int nch = H / 8;  // 16-byte chunks per row
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wg + static_cast<size_t>(e) * H, static_cast<uint32_t>(H) * 2u);
+  const uint32_t x_end = static_cast<uint32_t>(T) * H * 2u;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_end);
 
   float acc[kGemvMaxT];
 #pragma unroll
   for (int t = 0; t < kGemvMaxT; ++t) acc[t] = 0.f;
-  for (int base = 0; base < per_lane; base += kGemvWin) {
-    if (base > 0) load_window(base);
+  for (int base = 0; base < nch; base += 64 * kGemvWin) {
+    // chunks past the row read zeros (offsets at or past the buffer's end)
+    int c[kGemvWin];
+    uint4 w[kGemvWin];
 #pragma unroll
     for (int i = 0; i < kGemvWin; ++i) {
-      const int c = (base + i) * 64 + lane;
-      if (base + i < per_lane && c < nch) {
-#pragma unroll
-        for (int t = 0; t < kGemvMaxT; ++t)
-          if (t < T) acc[t] = dot8(w[i], xs[t * nch + c], acc[t]);
-      }
+      c[i] = base + i * 64 + lane;
+      w[i] = load_b128(rw, c[i] < nch ? static_cast<uint32_t>(c[i]) * 16u : static_cast<uint32_t>(H) * 2u);
     }
+    // tokens in halves of kGemvHalf: all of a half's x loads go out before
+    // its dot products
+    auto half = [&](auto t0_tag) {
+      constexpr int T0 = decltype(t0_tag)::value;
+      uint4 xv[kGemvHalf][kGemvWin];
+#pragma unroll
+      for (int tt = 0; tt < kGemvHalf; ++tt)
+#pragma unroll
+        for (int i = 0; i < kGemvWin; ++i) {
+          const bool in = T0 + tt < T && c[i] < nch;
+          xv[tt][i] = load_b128(rx, in ? (static_cast<uint32_t>(T0 + tt) * nch + c[i]) * 16u : x_end);
+        }
+#pragma unroll
+      for (int tt = 0; tt < kGemvHalf; ++tt)
+#pragma unroll
+        for (int i = 0; i < kGemvWin; ++i) acc[T0 + tt] = dot8(w[i], xv[tt][i], acc[T0 + tt]);
+    };
+    half(std::integral_constant<int, 0>{});
+    if (T > kGemvHalf) half(std::integral_constant<int, kGemvHalf>{});
   }
 #pragma unroll
   for (int t = 0; t < kGemvMaxT; ++t) {
     if (t < T) {
       const float v = wave_sum(acc[t]);
-      if (lane == t && e < E) logits[static_cast<size_t>(t) * E + e] = v;
+      if (lane == t) logits[static_cast<size_t>(t) * E + e] = v;
     }
   }
 }
@@ -214,11 +221,9 @@ __global__ __launch_bounds__(kMmThreads) void router_mfma_kernel(
 
 void launch_router_gate(const uint16_t* x, int T, int H, const uint16_t* gate_weight, int E,
                         float* logits, bool gemv, hipStream_t stream) {
-  if (gemv) {  // T <= kGemvMaxT and x in 80 KiB of LDS (the plan checks it)
-    const dim3 grid((E + kGemvWaves - 1) / kGemvWaves);
-    const size_t lds = static_cast<size_t>(T) * H * 2;
-    hipLaunchKernelGGL(router_gemv_kernel, grid, dim3(64 * kGemvWaves), lds, stream, x, T, H,
-                       gate_weight, E, logits);
+  if (gemv) {  // T <= kGemvMaxT (the plan checks it)
+    hipLaunchKernelGGL(router_gemv_kernel, dim3(E), dim3(64), 0, stream, x, T, H, gate_weight, E,
+                       logits);
     return;
   }
   const int n_m = (T + kTile - 1) / kTile, n_n = (E + kTile - 1) / kTile;
