@@ -785,6 +785,9 @@ def run_sweep(args, dev) -> dict:
         gw = torch.from_numpy(synth.make_gate_weight(full, args.seed)).to(dev)
         n = 16
         copies = device_copies(w0, n)
+        # the block with a shared expert (expert E of E + 1) up to the GEMV's 32 tokens
+        wsh = ops.weights_to_device(synth.make_weights(dataclasses.replace(full, E=E + 1), args.seed), dev)
+        copies_sh = device_copies(wsh, n)
         for T in tokens:
             logits = torch.from_numpy(act["logits"][:T]).to(dev)
             x = torch.from_numpy(np.ascontiguousarray(act["x"][:T])).to(dev)
@@ -828,8 +831,38 @@ def run_sweep(args, dev) -> dict:
                                  "plan": dict(base, router_gemv=gemv),
                                  "default": gemv == base["router_gemv"], "us": res[gemv]})
                 log(f"I={I} T={T} block: router GEMV {res[1]:.1f} us, MFMA {res[0]:.1f} us")
+            # the shared expert: on the matrix cores in extra workgroups of the
+            # GEMV, as one more expert of the GEMV, or the matrix-core FFN
+            base_sh = ops.plan_default(T, k, E, H, I, shared=True).as_dict()
+            if T <= 32:
+                logits_out = torch.empty((T, E), dtype=torch.float32, device=dev)
+                sh_ws = torch.empty(ops.block_workspace_bytes(T, k, E, True, H, I),
+                                    dtype=torch.uint8, device=dev)
+                gemv_sh = dict(base_sh, ffn=ops.FFN_GEMV, route=ops.ROUTE_IN_GATE_UP)
+                cands = {"GEMV, shared on matrix cores": dict(gemv_sh, shared_mfma=1),
+                         "GEMV, shared in it": dict(gemv_sh, shared_mfma=0),
+                         "matrix cores": dict(base_sh, ffn=ops.FFN_MFMA, shared_mfma=0,
+                                              route=ops.ROUTE_SEPARATE)}
+                res = {}
+                for tag, d in cands.items():
+                    plan = _plan(d)
+
+                    def sstep(i, plan=plan):
+                        ops.moe_block_forward_plan(x, gw, k, copies_sh[i % n], True, plan, sh_ws,
+                                                   logits_out, out)
+
+                    try:
+                        sstep(0)
+                    except ops.MoEError:
+                        continue  # refused before anything is enqueued (its A rows do not fit in LDS)
+                    res[tag] = avg_ms(sstep, steps, 2) * 1e3
+                    rows.append({"I": I, "T": T, "what": "block with shared expert", "plan": d,
+                                 "default": all(d[f] == base_sh[f] for f in ("ffn", "shared_mfma", "route")),
+                                 "us": res[tag]})
+                log(f"I={I} T={T} block with shared expert: "
+                    + ", ".join(f"{tag} {us:.1f} us" for tag, us in res.items()))
             del ws
-        del copies, w0
+        del copies, w0, copies_sh, wsh
         torch.cuda.empty_cache()
     # per (I, T): the default plan against the fastest one swept
     best = []

@@ -240,6 +240,7 @@ def _block_check(shape, seed, dev, dtype=np.float64):
     (128, 4, 512, 160, 32),     # and a full one
     (8, 2, 288, 96, 5),         # odd group counts: K splits of 3, 3, 3, 0 and 2, 1 groups
     (512, 10, 2560, 640, 3),    # the fewest tokens with the shared expert on the matrix cores
+    (512, 10, 2560, 640, 28),   # too many for its LDS: the matrix-core FFN takes the block
 ])
 def test_block_matches_oracle(dev, E, k, H, I, T):
     _block_check(_shape(E, k, H, I, T), 7, dev)

@@ -80,6 +80,12 @@ def test_rows_per_pass_and_cost_split():
     # workgroup's LDS: 22 rows of 2560 fit, 23 do not
     assert plan(22, shared=True)["shared_mfma"] == 1
     assert plan(23, shared=True)["shared_mfma"] == 0
+    # ... and then the matrix-core FFN takes the block (its rows one more M-tile)
+    assert plan(22, shared=True)["ffn"] == ops.FFN_GEMV
+    assert plan(23, shared=True)["ffn"] == ops.FFN_MFMA
+    assert plan(23, shared=True)["route"] == ops.ROUTE_SEPARATE
+    assert plan(32, shared=True)["ffn"] == ops.FFN_MFMA and plan(32)["ffn"] == ops.FFN_GEMV
+    assert plan(2, shared=True)["ffn"] == ops.FFN_GEMV   # below 3 tokens the GEMV holds it
     assert plan(8, H=16384, shared=True)["shared_mfma"] == 0
     assert plan(33, shared=True)["shared_mfma"] == 0          # matrix-core FFN: in its tile list
     assert plan(8)["shared_mfma"] == 0

@@ -90,9 +90,17 @@ Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
   p.rows_per_pass = T >= kRows4MinT ? 4 : (T >= 2 ? 2 : 1);
   p.cost_split = T >= kRows4MinT;
   p.router_gemv = T <= kRouterGemvMaxT && T * static_cast<int64_t>(H) * 2 <= kRouterGemvMaxXBytes;
+  // A shared expert of 3 tokens or more whose A rows do not fit in LDS (23
+  // and more at H = 2560): the matrix-core FFN, which takes its rows as one
+  // more M-tile (block, us, GEMV with the shared expert in it / matrix
+  // cores: I = 640: 23 tokens 259.3 / 203.6, 28: 293.1 / 222.5, 32: 297.5 /
+  // 230.7; I = 160: 23 tokens 189.3 / 113.2, 32: 199.7 / 117.0).
+  const bool shared_no_room =
+      shared && p.ffn == MOE_FFN_GEMV && T >= kSharedMfmaMinT && !p.shared_mfma;
   // the GEMV's A fragments of a long K (I near 16384 for the down stage)
   // do not fit a workgroup's LDS: the matrix cores then take every size
-  if (p.ffn == MOE_FFN_GEMV && !gemv_fits(p, T, top_k, E, shared, H, I, kGfx950LdsBytes)) {
+  if (p.ffn == MOE_FFN_GEMV &&
+      (shared_no_room || !gemv_fits(p, T, top_k, E, shared, H, I, kGfx950LdsBytes))) {
     p.ffn = MOE_FFN_MFMA;
     p.shared_mfma = 0;
     if (p.route == MOE_ROUTE_IN_GATE_UP)
