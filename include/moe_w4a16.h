@@ -362,7 +362,8 @@ size_t moe_block_workspace_bytes(int64_t T, int32_t top_k, int32_t E,
  * the shared expert in the FFN's kernels (shared_mfma = 0); the default at
  * GEMV sizes from 3 tokens runs its rows on the matrix cores in extra
  * workgroups of the same launches (shared_mfma = 1), which changes the order
- * of its fp32 sums only.  Sections as moe_router_gate and moe_route_shared.
+ * of its fp32 sums only, and where those rows do not fit in LDS (23 to 32
+ * tokens at H = 2560) takes the matrix-core FFN instead.  Sections as moe_router_gate and moe_route_shared.
  *
  *   x            in   fp16 [T, H]
  *   gate_weight  in   fp16 [E, H]
