@@ -226,6 +226,11 @@ def test_token_counts(dev, T):
     (4, 2, 8192, 64, 4),      # decode, long K of gate/up: 32 steps per row block
     (4, 2, 128, 4096, 3),     # decode, long K of down: 16 steps per row block
     (6, 3, 96, 96, 2),        # decode, odd group counts: one lane per row
+    (2, 1, 16384, 64, 2),     # largest H, decode GEMV
+    (2, 1, 64, 16384, 2),     # largest I at decode size: the down GEMV's A rows do not
+                              # fit in LDS, so the matrix-core kernels take it
+    (2, 2, 16384, 64, 40),    # largest H, matrix cores
+    (2, 2, 64, 16384, 40),    # largest I, matrix cores
 ])
 def test_degenerate_shapes(dev, E, k, H, I, T):
     _full_check(synth.MoEShape(E=E, top_k=k, H=H, I=I, T=T), 5, dev)
