@@ -728,7 +728,7 @@ def candidate_plans(T: int, E: int, k: int, H: int, I: int) -> list:
     from w4a16_group_quantized_amd import ops
 
     base = ops.plan_default(T, k, E, H, I).as_dict()
-    lanes = lambda G: [c for c in (1, 2, 4, 8) if G % c == 0]  # noqa: E731
+    lanes = lambda G: [c for c in (1, 2, 4, 8, 16) if G % c == 0]  # noqa: E731
     out = []
     if T <= 64:
         gemv = dict(base, ffn=ops.FFN_GEMV, rows_per_pass=2 if T >= 2 else 1, cost_split=0)

@@ -407,8 +407,8 @@ typedef struct moe_plan {
   int32_t ffn;            /* MOE_FFN_GEMV or MOE_FFN_MFMA                            */
   int32_t route;          /* MOE_ROUTE_*                                              */
   int32_t msub;           /* MFMA: 32-row subtiles per M-tile, 1 or 4                 */
-  int32_t lanes_gate_up;  /* GEMV: lanes per w13 row, 1/2/4/8 dividing H/32           */
-  int32_t lanes_down;     /* GEMV: lanes per w2 row, 1/2/4/8 dividing I/32            */
+  int32_t lanes_gate_up;  /* GEMV: lanes per w13 row, 1/2/4/8/16 dividing H/32        */
+  int32_t lanes_down;     /* GEMV: lanes per w2 row, 1/2/4/8/16 dividing I/32         */
   int32_t rows_per_pass;  /* GEMV: A rows of an expert per weight pass, 1/2/4/8
                              (the down stage takes at most 4)                         */
   int32_t cost_split;     /* GEMV: 1 share work out by cost (rows per expert), 0 evenly */

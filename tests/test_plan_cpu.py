@@ -51,6 +51,11 @@ def test_m_tile_switches_at_64_rows_per_expert():
 
 def test_lanes_per_row_divide_the_groups():
     assert plan(8)["lanes_gate_up"] == 8     # H = 2560: 80 groups
+    assert plan(5)["lanes_gate_up"] == 8
+    assert plan(4)["lanes_gate_up"] == 16    # up to 4 tokens: 16 lanes where they divide
+    assert plan(1, I=160)["lanes_gate_up"] == 16
+    assert plan(4, H=2592)["lanes_gate_up"] == 1   # 81 groups
+    assert plan(4, H=2624)["lanes_gate_up"] == 2   # 82 groups
     assert plan(8)["lanes_down"] == 4        # I = 640: 20 groups
     assert plan(8, I=160)["lanes_down"] == 1  # 5 groups
     assert plan(8, I=64)["lanes_down"] == 2   # 2 groups
@@ -124,6 +129,8 @@ def test_layer_rejects_plans_the_sizes_do_not_allow():
     assert _layer(lib, dict(base, msub=2)) == ops.MOE_ERR_INVALID_ARG
     assert _layer(lib, dict(base, lanes_gate_up=3)) == ops.MOE_ERR_INVALID_ARG
     assert _layer(lib, dict(base, lanes_down=8)) == ops.MOE_ERR_INVALID_ARG   # 20 groups
+    assert _layer(lib, dict(base, lanes_down=16)) == ops.MOE_ERR_INVALID_ARG  # 20 groups
+    assert _layer(lib, dict(base, lanes_gate_up=32)) == ops.MOE_ERR_INVALID_ARG
     assert _layer(lib, dict(base, ffn=2)) == ops.MOE_ERR_INVALID_ARG
     assert _layer(lib, dict(base, route=3)) == ops.MOE_ERR_INVALID_ARG
     assert _layer(lib, dict(base, rows_per_pass=3)) == ops.MOE_ERR_INVALID_ARG

@@ -1022,7 +1022,7 @@ size_t shared_mfma_lds(int64_t T, int H, int I) {
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream) {
   Geom geo{};
   geo.G = a.H / kGroup;
-  geo.C = a.lanes;  // a power of two <= 8 dividing G (the plan)
+  geo.C = a.lanes;  // a power of two <= 16 dividing G (the plan)
   geo.spb = geo.G / geo.C;
   const int half = (64 / geo.C) / 2;  // gate (= up) rows per block
   geo.nb = (a.I + half - 1) / half;

@@ -49,12 +49,17 @@ constexpr int64_t kRouterGemvMaxXBytes = 80 * 1024;
 // 47.0, 3: 59.5 / 67.6, 4: 64.8 / 85.4, 16: 130.7 / 160.7; I = 160: 1 token
 // 41.1 / 31.9, 2: 46.0 / 35.5, 3: 49.4 / 50.7.
 constexpr int64_t kSharedMfmaMinT = 3;
+// 16 lanes per w13 row up to 4 tokens (each wave's run of loads per block is
+// half as long), 8 above (layer, us, 8 / 16 lanes: I = 160: 1 token 26.9 /
+// 25.5, 2: 28.7 / 27.7, 4: 33.6 / 32.9, 8: 40.5 / 40.2, 16: 67.6 / 69.0;
+// I = 640: 1 token 30.9 / 30.2, 4: 48.7 / 48.0, 8: 69.2 / 71.8).
+constexpr int64_t kLanes16MaxT = 4;
 
 // Lanes per weight row of a GEMV over K = 32 G: the largest power of two
-// <= 8 that divides G (a lane takes every lanes-th group of the row).
-static int gemv_lanes(int G) {
+// <= cap that divides G (a lane takes every lanes-th group of the row).
+static int gemv_lanes(int G, int cap) {
   int C = 1;
-  while (C < 8 && G % (2 * C) == 0) C *= 2;
+  while (C < cap && G % (2 * C) == 0) C *= 2;
   return C;
 }
 
@@ -80,8 +85,8 @@ Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
   else
     p.route = MOE_ROUTE_SEPARATE;
   p.msub = S >= kMsub4RowsPerExpert * static_cast<int64_t>(EP) ? 4 : 1;
-  p.lanes_gate_up = gemv_lanes(H / kGroup);
-  p.lanes_down = gemv_lanes(I / kGroup);
+  p.lanes_gate_up = gemv_lanes(H / kGroup, T <= kLanes16MaxT ? 16 : 8);
+  p.lanes_down = gemv_lanes(I / kGroup, 8);
   // A shared expert with the GEMV runs on the matrix cores in extra
   // workgroups (the GEMV then holds the routed experts only) from 3 tokens,
   // where its A rows fit in LDS.
@@ -129,7 +134,9 @@ int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, in
   if (p.cost_split != 0 && p.cost_split != 1) return MOE_ERR_INVALID_ARG;
   if (p.route < MOE_ROUTE_IN_GATE_UP || p.route > MOE_ROUTE_SEPARATE) return MOE_ERR_INVALID_ARG;
   if (p.msub != 1 && p.msub != 4) return MOE_ERR_INVALID_ARG;
-  auto lanes_ok = [](int c, int G) { return (c == 1 || c == 2 || c == 4 || c == 8) && G % c == 0; };
+  auto lanes_ok = [](int c, int G) {
+    return (c == 1 || c == 2 || c == 4 || c == 8 || c == 16) && G % c == 0;
+  };
   if (!lanes_ok(p.lanes_gate_up, H / kGroup) || !lanes_ok(p.lanes_down, I / kGroup))
     return MOE_ERR_INVALID_ARG;
   if (p.router_gemv != 0 && p.router_gemv != 1) return MOE_ERR_INVALID_ARG;
