@@ -25,9 +25,13 @@
 // (0, 4, 1, 5, 2, 6, 3, 7), the order in which the nibble unpack produces
 // (q - z) pairs, so A is stored permuted the same way: x by a pre-pass, act
 // by the stage-1 epilogue.  A lane of half h of the wave supplies, for MFMA t
-// of a group, 8-value block 2h + t.  The two wave halves load the codes of
-// two consecutive groups (16 bytes per lane), and two v_permlane32_swap
-// exchanges give every lane its two blocks of each group.  Stage 2 runs
+// of a group, 8-value block 2h + t.  Stage 2: the two wave halves load the
+// codes of two consecutive groups (16 bytes per lane), and two
+// v_permlane32_swap exchanges give every lane its two blocks of each group.
+// Stage 1: kKC lanes read a row's kKC consecutive groups (so one load
+// instruction covers 64 / kKC rows of contiguous bytes instead of 32 rows of
+// 32 bytes), and each wave passes its codes through a private LDS area from
+// which every lane reads its two blocks of each group.  Stage 2 runs
 // act_hi and act_lo through the same partial (act carried at about 22 bits).
 //
 // Staging.  A rows go through LDS in fragment order (one 1 KiB block per
@@ -65,6 +69,20 @@ template <bool GATE_UP, int MSUB>
 struct StageCfg {
   static constexpr int kCopies = GATE_UP ? 1 : 2;   // A copies: x, or act hi + lo
   static constexpr int kKC = (GATE_UP ? 4 : 2) * (MSUB == 1 ? 2 : 1);
+  // codes through LDS (stage 1; 1024 tokens: gate/up 304 us against 328 with
+  // the lane-half loads and swaps; stage 2 kept the swaps: the LDS area cost
+  // its 32-row kernel a workgroup per compute unit, 212 against 198 us)
+  static constexpr bool kCodesLds = GATE_UP;
+};
+
+// Per-wave LDS copy of a stage's codes: 32 rows of KC groups (16 bytes each),
+// row stride KC x 16 + 8 bytes, so that the 32 rows' 8-byte reads of one
+// group fall on distinct banks (the stride in banks, 4 KC + 2, is twice an
+// odd number).
+template <int KC>
+struct CodesLds {
+  static constexpr int kStride = KC * 16 + 8;
+  static constexpr int kWaveBytes = 32 * kStride;
 };
 
 struct PrefillArgs {
@@ -101,10 +119,11 @@ struct BRegs {
 
 struct BAddr {
   __amdgpu_buffer_rsrc_t rq, rs, rz;
-  uint32_t q_row, s_row, z_row;       // byte offsets of the first group of the lane's row
+  uint32_t q_rows[4];                 // codes: first byte of the row of load pp
+  uint32_t qg;                        // codes: group of load pp, less 2 pp (lane swaps)
+  uint32_t s_row, z_row;              // byte offsets of the first group of the lane's row
   uint32_t q_oob, s_oob, z_oob;       // offsets that read as zero
   int G;
-  int h;                              // lane half
 };
 
 // Loads of one stage's weight operands.  The whole byte offset of every load
@@ -115,14 +134,15 @@ struct BAddr {
 // last valid groups, which the compute skips.  VEC (the group count is a
 // multiple of kKC): a stage's zero words and scales of one row are contiguous
 // and aligned, and are read with one wide load each.
-template <int KC, bool VEC>
+template <int KC, bool VEC, bool CODES_LDS>
 __device__ __forceinline__ void load_b_stage(const BAddr& ba, int g0, BRegs<KC>& b) {
 #pragma unroll
   for (int pp = 0; pp < KC / 2; ++pp) {
-    // lane half h loads group g0 + 2 pp + h of its own row (ba.q_row is the
-    // row's first byte)
-    const uint32_t g = static_cast<uint32_t>(min(g0 + 2 * pp + ba.h, ba.G - 1));
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rq, static_cast<int>(ba.q_row + g * 16u), 0, 0);
+    // lane swaps: lane half h loads group g0 + 2 pp + h of its own row;
+    // codes through LDS: group g0 + L % KC of row 64 / KC pp + L / KC
+    const int gl = g0 + static_cast<int>(ba.qg) + (CODES_LDS ? 0 : 2 * pp);
+    const uint32_t g = static_cast<uint32_t>(min(gl, ba.G - 1));
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(ba.rq, static_cast<int>(ba.q_rows[pp] + g * 16u), 0, 0);
     b.q[pp] = make_uint4(v[0], v[1], v[2], v[3]);
   }
   if constexpr (VEC) {
@@ -235,13 +255,25 @@ __device__ __forceinline__ void store_a(uint32_t tid, const AStage<GATE_UP, MSUB
     }
 }
 
+// A stage's codes (as loaded for CodesLds) into the wave's LDS area.
+template <int KC>
+__device__ __forceinline__ void write_codes(uint32_t tid, const BRegs<KC>& b, uint8_t* cw) {
+  const int lane = static_cast<int>(tid & 63);
+#pragma unroll
+  for (int pp = 0; pp < KC / 2; ++pp) {
+    uint8_t* d = cw + CodesLds<KC>::kStride * ((64 / KC) * pp + lane / KC) + 16 * (lane % KC);
+    *reinterpret_cast<uint2*>(d) = make_uint2(b.q[pp].x, b.q[pp].y);
+    *reinterpret_cast<uint2*>(d + 8) = make_uint2(b.q[pp].z, b.q[pp].w);
+  }
+}
+
 // One stage of the main loop: NG groups (NG < kKC only in a tail stage) of a
 // tile with NS live 32-row subtiles.  The scaling of each partial is issued
 // after the next partial's MFMAs, so it does not wait on its own MFMA.
 template <bool GATE_UP, int MSUB, int NS, int NG>
 __device__ __forceinline__ void compute_stage(uint32_t tid, const uint16_t* stage,
                                               const BRegs<StageCfg<GATE_UP, MSUB>::kKC>& b,
-                                              uint32_t zshift, uint32_t bias,
+                                              const uint8_t* cw, uint32_t zshift, uint32_t bias,
                                               float16v (&acc)[MSUB]) {
   constexpr int KC = StageCfg<GATE_UP, MSUB>::kKC;
   constexpr int kLoOff = KC * MSUB * 2 * kBlockHalfs;   // act_lo copy
@@ -250,11 +282,22 @@ __device__ __forceinline__ void compute_stage(uint32_t tid, const uint16_t* stag
   float pend_s = 0.f;
 #pragma unroll
   for (int pp = 0; pp < (NG + 1) / 2; ++pp) {
-    // lane half 0 holds group 2pp, half 1 group 2pp + 1; after the swaps the
-    // lower half holds words 0 and 1 and the upper half words 2 and 3 of each
-    const auto sx = __builtin_amdgcn_permlane32_swap(b.q[pp].x, b.q[pp].z, false, false);
-    const auto sy = __builtin_amdgcn_permlane32_swap(b.q[pp].y, b.q[pp].w, false, false);
-    const uint32_t words[2][2] = {{sx[0], sy[0]}, {sx[1], sy[1]}};   // [group][MFMA]
+    // lane half h needs words 2 h and 2 h + 1 of groups 2 pp and 2 pp + 1
+    // of its row
+    uint32_t words[2][2];   // [group][MFMA]
+    if constexpr (StageCfg<GATE_UP, MSUB>::kCodesLds) {
+      const int jj = lane & 31, hh = lane >> 5;
+      const uint8_t* r = cw + CodesLds<KC>::kStride * jj + 8 * hh;
+      const uint2 w0 = *reinterpret_cast<const uint2*>(r + 16 * (2 * pp));
+      const uint2 w1 = *reinterpret_cast<const uint2*>(r + 16 * (2 * pp + 1));
+      words[0][0] = w0.x; words[0][1] = w0.y; words[1][0] = w1.x; words[1][1] = w1.y;
+    } else {
+      // lane half 0 holds group 2pp, half 1 group 2pp + 1; after the swaps
+      // the lower half holds words 0 and 1 and the upper half words 2 and 3
+      const auto sx = __builtin_amdgcn_permlane32_swap(b.q[pp].x, b.q[pp].z, false, false);
+      const auto sy = __builtin_amdgcn_permlane32_swap(b.q[pp].y, b.q[pp].w, false, false);
+      words[0][0] = sx[0]; words[0][1] = sy[0]; words[1][0] = sx[1]; words[1][1] = sy[1];
+    }
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const int g = 2 * pp + gi;
@@ -302,11 +345,11 @@ __device__ __forceinline__ void compute_stage(uint32_t tid, const uint16_t* stag
 template <bool GATE_UP, int MSUB, int NS, int NG>
 __device__ __forceinline__ void compute_tail(uint32_t tid, int ng, const uint16_t* stage,
                                              const BRegs<StageCfg<GATE_UP, MSUB>::kKC>& b,
-                                             uint32_t zshift, uint32_t bias,
+                                             const uint8_t* cw, uint32_t zshift, uint32_t bias,
                                              float16v (&acc)[MSUB]) {
   if constexpr (NG >= 1) {
-    if (ng == NG) compute_stage<GATE_UP, MSUB, NS, NG>(tid, stage, b, zshift, bias, acc);
-    else compute_tail<GATE_UP, MSUB, NS, NG - 1>(tid, ng, stage, b, zshift, bias, acc);
+    if (ng == NG) compute_stage<GATE_UP, MSUB, NS, NG>(tid, stage, b, cw, zshift, bias, acc);
+    else compute_tail<GATE_UP, MSUB, NS, NG - 1>(tid, ng, stage, b, cw, zshift, bias, acc);
   }
 }
 
@@ -319,31 +362,39 @@ __device__ __forceinline__ void main_loop(uint32_t tid, const ASrc& asrc, uint16
   const int G = ba.G;
   uint32_t bias;   // kept in a vector register so each mask-and-insert is one v_and_or_b32
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(bias));
+  constexpr bool CL = StageCfg<GATE_UP, MSUB>::kCodesLds;
   const int nfull = G / KC;
   BRegs<KC> bcur, bnxt;
   AStage<GATE_UP, MSUB> astage;
-  load_b_stage<KC, VEC>(ba, 0, bcur);
+  // the wave's codes area (stage 1), after the two A stages
+  uint8_t* const cw = reinterpret_cast<uint8_t*>(lds + 2 * S::kStageHalfs) +
+                      (static_cast<int>(tid >> 6) & (kWaves - 1)) * CodesLds<KC>::kWaveBytes;
+  load_b_stage<KC, VEC, CL>(ba, 0, bcur);
   load_a<GATE_UP, MSUB, NS>(tid, asrc, 0, G, astage);
   store_a<GATE_UP, MSUB, NS>(tid, astage, lds);
+  if constexpr (CL) write_codes<KC>(tid, bcur, cw);
   __syncthreads();
   for (int s = 0; s < nfull; ++s) {
     const int g0 = s * KC;
     // The next stage's loads are issued unconditionally (past the end of K
     // they read zeros or the following row), so every wait below is exact.
-    load_b_stage<KC, VEC>(ba, g0 + KC, bnxt);
+    load_b_stage<KC, VEC, CL>(ba, g0 + KC, bnxt);
     load_a<GATE_UP, MSUB, NS>(tid, asrc, g0 + KC, G, astage);
     // keep the loads ahead of the compute that hides their latency
     __builtin_amdgcn_sched_barrier(0);
-    compute_stage<GATE_UP, MSUB, NS, KC>(tid, lds + (s & 1) * S::kStageHalfs, bcur, zshift, bias,
-                                         acc);
+    compute_stage<GATE_UP, MSUB, NS, KC>(tid, lds + (s & 1) * S::kStageHalfs, bcur, cw, zshift,
+                                         bias, acc);
     __builtin_amdgcn_sched_barrier(0);
     store_a<GATE_UP, MSUB, NS>(tid, astage, lds + ((s + 1) & 1) * S::kStageHalfs);
+    // the same wave read this stage's codes above: its LDS operations stay
+    // in order, so no barrier is needed before overwriting them
+    if constexpr (CL) write_codes<KC>(tid, bnxt, cw);
     bcur = bnxt;
     __syncthreads();
   }
   // tail stage of G % KC groups, loaded by the last iteration
   compute_tail<GATE_UP, MSUB, NS, KC - 1>(tid, G - nfull * KC, lds + (nfull & 1) * S::kStageHalfs,
-                                          bcur, zshift, bias, acc);
+                                          bcur, cw, zshift, bias, acc);
 }
 
 // One work item: M-tile `slot` of the tile list against N-tile `nt`.
@@ -402,7 +453,6 @@ __device__ __forceinline__ void process_item(const PrefillArgs& p, int slot, int
   const bool n_ok = n < N;
   BAddr ba;
   ba.G = G;
-  ba.h = h;
   ba.rq = make_rsrc(p.qw + wbase * (G * 4), static_cast<uint32_t>(N) * G * 16u);
   ba.rs = make_rsrc(p.sc + wbase * G, static_cast<uint32_t>(N) * G * 2u);
   ba.rz = make_rsrc(p.qz + (wbase / 8) * G, static_cast<uint32_t>(N / 8) * G * 4u);
@@ -410,7 +460,23 @@ __device__ __forceinline__ void process_item(const PrefillArgs& p, int slot, int
   ba.s_oob = static_cast<uint32_t>(N) * G * 2u;
   ba.z_oob = static_cast<uint32_t>(N / 8) * G * 4u;
   // a lane past the matrix reads from the end of the buffers: zeros
-  ba.q_row = n_ok ? static_cast<uint32_t>(n) * G * 16u : ba.q_oob;
+  {
+    constexpr int KC = StageCfg<GATE_UP, MSUB>::kKC;
+    if constexpr (StageCfg<GATE_UP, MSUB>::kCodesLds) {
+      // load pp of lane L: group L % KC of the wave's row 64 / KC pp + L / KC
+      ba.qg = static_cast<uint32_t>(lane % KC);
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int jr = (64 / KC) * pp + lane / KC;
+        const int nr = c0 < p.I ? (jr < 16 ? c0 + jr : p.I + c0 + jr - 16) : N;
+        ba.q_rows[pp] = (pp < KC / 2 && nr < N) ? static_cast<uint32_t>(nr) * G * 16u : ba.q_oob;
+      }
+    } else {
+      ba.qg = static_cast<uint32_t>(h);
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) ba.q_rows[pp] = n_ok ? static_cast<uint32_t>(n) * G * 16u : ba.q_oob;
+    }
+  }
   ba.s_row = n_ok ? static_cast<uint32_t>(n) * G * 2u : ba.s_oob;
   ba.z_row = n_ok ? static_cast<uint32_t>(n >> 3) * G * 4u : ba.z_oob;
   const uint32_t zshift = 4u * static_cast<uint32_t>(n & 7);
@@ -475,7 +541,9 @@ template <bool GATE_UP, int MSUB, bool VEC>
 __global__ __launch_bounds__(kThreads) void ffn_mfma_kernel(PrefillArgs p, int n_ntiles,
                                                             const int* __restrict__ sched) {
   using S = AStage<GATE_UP, MSUB>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::kStageHalfs];
+  constexpr int kCodesBytes =
+      StageCfg<GATE_UP, MSUB>::kCodesLds ? kWaves * CodesLds<S::kKC>::kWaveBytes : 0;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::kStageHalfs + kCodesBytes / 2];
   const int x = static_cast<int>(blockIdx.x & 7);
   const int item = sched[x] + static_cast<int>(blockIdx.x >> 3);
   if (item >= sched[x + 1]) return;
