@@ -236,6 +236,30 @@ def test_degenerate_shapes(dev, E, k, H, I, T):
     _full_check(synth.MoEShape(E=E, top_k=k, H=H, I=I, T=T), 5, dev)
 
 
+def _random_shapes(n, seed, t_max):
+    """Seeded shapes across the supported ranges, small enough for the oracle
+    (E * 2I * H at most 2^24 weights)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.integers(1, 300))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        H = 32 * int(rng.integers(1, 41))
+        I = 32 * int(rng.integers(1, 41))
+        T = int(rng.integers(1, t_max + 1))
+        if E * 2 * I * H <= 1 << 24:
+            out.append((E, k, H, I, T))
+    return out
+
+
+# up to 300 tokens (mostly the matrix-core kernels), then up to 32 (the GEMV)
+@pytest.mark.parametrize("E,k,H,I,T", _random_shapes(16, 2024, 300) + _random_shapes(10, 7, 32))
+def test_random_shapes(dev, E, k, H, I, T):
+    """Seeded random sizes (any E, top-k, H and I multiples of 32, T up to
+    300): every output against the oracle, on whatever plan the table picks."""
+    _full_check(synth.MoEShape(E=E, top_k=k, H=H, I=I, T=T), 11, dev)
+
+
 def test_every_token_on_one_expert(dev):
     shape = synth.MoEShape(E=32, top_k=4, H=256, I=128, T=200)
     host = synth.make_inputs(shape, 9)
