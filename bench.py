@@ -731,7 +731,8 @@ def candidate_plans(T: int, E: int, k: int, H: int, I: int) -> list:
     lanes = lambda G: [c for c in (1, 2, 4, 8, 16) if G % c == 0]  # noqa: E731
     out = []
     if T <= 64:
-        gemv = dict(base, ffn=ops.FFN_GEMV, rows_per_pass=2 if T >= 2 else 1, cost_split=0)
+        gemv = dict(base, ffn=ops.FFN_GEMV, rows_per_pass=2 if T >= 2 else 1, cost_split=0,
+                    combine_in_down=0)
         # lanes per row, with either routing form
         for route in ((ops.ROUTE_IN_GATE_UP, ops.ROUTE_ONE_LAUNCH) if E <= 1024
                       else (ops.ROUTE_SEPARATE,)):
@@ -745,12 +746,18 @@ def candidate_plans(T: int, E: int, k: int, H: int, I: int) -> list:
         for rows in (2, 4, 8):
             if rows <= max(2, T):
                 for cost in (0, 1):
-                    out.append(dict(gemv, route=route, rows_per_pass=rows, cost_split=cost))
+                    out.append(dict(gemv, route=route, rows_per_pass=rows, cost_split=cost,
+                                    combine_in_down=0))
+        # the combine folded into the down GEMV (up to 2 tokens), with the
+        # default lanes and rows per pass
+        if T <= 2:
+            for fold in (0, 1):
+                out.append(dict(base, ffn=ops.FFN_GEMV, route=route, combine_in_down=fold))
     routes = (ops.ROUTE_ONE_LAUNCH, ops.ROUTE_SEPARATE) if T <= 64 and E <= 1024 else (
         ops.ROUTE_SEPARATE,)
     for msub in (1, 4):
         for route in routes:
-            out.append(dict(base, ffn=ops.FFN_MFMA, route=route, msub=msub))
+            out.append(dict(base, ffn=ops.FFN_MFMA, route=route, msub=msub, combine_in_down=0))
     uniq = []
     for d in out:
         if d not in uniq:
@@ -839,10 +846,11 @@ def run_sweep(args, dev) -> dict:
                 sh_ws = torch.empty(ops.block_workspace_bytes(T, k, E, True, H, I),
                                     dtype=torch.uint8, device=dev)
                 gemv_sh = dict(base_sh, ffn=ops.FFN_GEMV, route=ops.ROUTE_IN_GATE_UP)
-                cands = {"GEMV, shared on matrix cores": dict(gemv_sh, shared_mfma=1),
+                cands = {"GEMV, shared on matrix cores": dict(gemv_sh, shared_mfma=1,
+                                                              combine_in_down=0),
                          "GEMV, shared in it": dict(gemv_sh, shared_mfma=0),
                          "matrix cores": dict(base_sh, ffn=ops.FFN_MFMA, shared_mfma=0,
-                                              route=ops.ROUTE_SEPARATE)}
+                                              route=ops.ROUTE_SEPARATE, combine_in_down=0)}
                 res = {}
                 for tag, d in cands.items():
                     plan = _plan(d)

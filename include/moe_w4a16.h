@@ -418,6 +418,13 @@ typedef struct moe_plan {
                              T x H and 2 T x I fp16 A rows and their K-split partial
                              sums in one workgroup's LDS: T <= 22 at H = 2560),
                              0 in the GEMV with the routed experts                    */
+  int32_t combine_in_down; /* layer and block calls with the GEMV, up to 2 tokens: 1
+                             the down launch also writes out (each workgroup takes
+                             one block of output rows of every active expert and
+                             combines it; needs shared_mfma = 0, I/32/lanes_down
+                             <= 8 and every act row's fragments in LDS), 0 a
+                             separate combine launch; the output is the same bit
+                             for bit                                                  */
 } moe_plan;
 
 /*

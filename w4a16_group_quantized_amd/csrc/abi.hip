@@ -532,8 +532,15 @@ static int layer_run(const float* logits, const uint16_t* x, int64_t T, int32_t 
                          pl.route == MOE_ROUTE_ONE_LAUNCH, st);
     run_gate_up(a, pl, w.ffn, st);
   }
+  if (pl.combine_in_down) {  // the down GEMV writes out itself
+    d.combine = 1;
+    d.c_weights = w.weights;
+    d.c_slot_rows = w.slot_rows;
+    d.out = out;
+  }
   run_down(d, pl, w.ffn, st);
-  launch_combine(w.y, w.weights, w.slot_rows, static_cast<int>(T), kk, H, out, st);
+  if (!pl.combine_in_down)
+    launch_combine(w.y, w.weights, w.slot_rows, static_cast<int>(T), kk, H, out, st);
   return check_launch();
 }
 

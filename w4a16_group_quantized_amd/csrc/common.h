@@ -108,6 +108,12 @@ struct DownArgs {
   const uint16_t* sc;
   const int* qz;
   float* y;
+  // the combine folded into the down GEMV (layer calls): out written from
+  // the weights and slot rows of the routing
+  int combine = 0;
+  const float* c_weights = nullptr;
+  const int* c_slot_rows = nullptr;
+  uint16_t* out = nullptr;
 };
 void launch_gate_up_decode(const GateUpArgs& a, const FfnWorkspace& ws, hipStream_t stream);
 
@@ -133,6 +139,11 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
 // device gives a workgroup cannot run.
 size_t gemv_min_lds(bool gate_up, bool route, int64_t T, int top_k, int E, int H, int I,
                     int lanes, bool cost_split);
+// The down GEMV with the combine folded in (T <= 2): its LDS (every act row's
+// fragments and one block of y rows), and whether it can run at these sizes
+// (at most 8 steps per lane, LDS within lds_bytes).
+size_t down_fold_lds(int64_t T, int top_k, int I, int lanes);
+bool down_fold_ok(int64_t T, int top_k, int I, int lanes, size_t lds_bytes);
 // LDS of the shared expert's matrix-core workgroups inside the GEMV launches
 // (A rows of both stages and the K-split partial sums), T <= 32.
 size_t shared_mfma_lds(int64_t T, int H, int I);

@@ -288,6 +288,11 @@ struct DecodeArgs {
   int* r_slot_rows;
   int* r_active;
   int* r_num_active;
+  // stage 2 with the combine folded in (down_fold_kernel): the routing's
+  // weights and slot rows in, the layer output out
+  const float* c_weights;
+  const int* c_slot_rows;
+  uint16_t* out;
 };
 
 // LDS bytes of the routing tables of a kernel that routes (T <= 64 tokens,
@@ -895,6 +900,103 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   }
 }
 
+// Stage 2 with the combine folded in, for T <= 2 tokens (an expert then holds
+// one or two rows): workgroup b takes block b (R = 64 / C output rows) of
+// every active expert, so the block's y rows of every token end up in one
+// workgroup.  All S = T top_k act rows are staged in LDS once; wave w takes
+// the active experts w, w + 8, ...; each lane cluster issues all spb loads of
+// its row before using any.  The rows' sums are the stage-2 GEMV's, in the
+// same order, bit for bit; they go to y_sorted and to LDS, where the
+// workgroup then adds each token's rows with the router weights, j ascending
+// from zero, and rounds once to fp16 (the combine kernel's order).
+constexpr int kFoldMaxSpb = 8;   // steps per lane held in registers
+constexpr int kFoldWaves = 8;    // 512 threads: 256 registers a lane for the held steps
+constexpr int kFoldThreads = 64 * kFoldWaves;
+
+__global__ __launch_bounds__(kFoldThreads) void down_fold_kernel(DecodeArgs p, Geom geo) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  const int G = geo.G, C = geo.C, spb = geo.spb;
+  const int H = p.H, I = p.I;
+  const int R = 64 / C;
+  const int S = p.T * p.top_k;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k = lane / C, lc = lane & (C - 1);
+  const int b = static_cast<int>(blockIdx.x);
+  uint32_t* frags = lds;  // [S][hi, lo][G]
+  float* ybuf = reinterpret_cast<float*>(frags + static_cast<size_t>(S) * 2 * G * kFragDwords);
+  for (int i = threadIdx.x; i < S * 2 * G; i += kFoldThreads) {
+    const int rf = i / G;  // row r = rf / 2, hi (0) or lo (1) = rf % 2
+    const int g = i - rf * G;
+    const uint16_t* src = ((rf & 1) ? p.a_lo : p.a_hi) + static_cast<size_t>(rf >> 1) * I;
+    stage_frag(src + 32 * g, frags + i * kFragDwords);
+  }
+  __syncthreads();
+  const int n_active = *p.num_active;
+  const int n = b * R + k;
+  const uint32_t row = n < H ? static_cast<uint32_t>(n) : static_cast<uint32_t>(H);  // past: zeros
+  for (int a = wave; a < n_active; a += kFoldWaves) {
+    const int e = p.active[a];
+    const int r0 = p.offsets[e];
+    const int nr = min(2, p.offsets[e + 1] - r0);
+    const ExpertBufs bufs = expert_bufs(p, H, G, e);
+    Slot sl[kFoldMaxSpb];
+    uint32_t sh[kFoldMaxSpb];
+#pragma unroll
+    for (int j = 0; j < kFoldMaxSpb; ++j) {
+      if (j < spb) {
+        const int gg = j * C + lc;
+        issue_step(bufs, G, row, gg, sl[j]);
+        sh[j] = __builtin_amdgcn_raw_buffer_load_b16(
+            bufs.s, static_cast<int>((row * static_cast<uint32_t>(G) + gg) * 2u), 0, 0);
+      }
+    }
+    float acc0 = 0.f, acc1 = 0.f;
+    const uint32_t* f0 = frags + static_cast<size_t>(r0) * 2 * G * kFragDwords;
+    const uint32_t* f1 = f0 + 2 * G * kFragDwords;
+#pragma unroll
+    for (int j = 0; j < kFoldMaxSpb; ++j) {
+      if (j < spb) {
+        const int gg = j * C + lc;
+        const float scale = half_bits_to_float(static_cast<uint16_t>(sh[j]));
+        const float z = static_cast<float>((sl[j].zw >> (4u * (row & 7u))) & 0xFu);
+        const Codes codes = expand_codes(sl[j].q);
+        float d0 = group_dot(codes, z, read_frag(f0 + gg * kFragDwords));
+        d0 += group_dot(codes, z, read_frag(f0 + (G + gg) * kFragDwords));
+        acc0 = fmaf(scale, d0, acc0);
+        if (nr > 1) {
+          float d1 = group_dot(codes, z, read_frag(f1 + gg * kFragDwords));
+          d1 += group_dot(codes, z, read_frag(f1 + (G + gg) * kFragDwords));
+          acc1 = fmaf(scale, d1, acc1);
+        }
+      }
+    }
+    const float v0 = cluster_sum(acc0, C);
+    const float v1 = cluster_sum(acc1, C);
+    if (lc == 0 && n < H) {
+      p.y[static_cast<size_t>(r0) * H + n] = v0;
+      ybuf[r0 * R + k] = v0;
+      if (nr > 1) {
+        p.y[static_cast<size_t>(r0 + 1) * H + n] = v1;
+        ybuf[(r0 + 1) * R + k] = v1;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = static_cast<int>(threadIdx.x); i < p.T * R; i += kFoldThreads) {
+    const int t = i / R;
+    const int r = i - t * R;
+    if (b * R + r < H) {
+      float acc = 0.f;
+      for (int j = 0; j < p.top_k; ++j) {
+        const int sl = t * p.top_k + j;
+        acc = fmaf(p.c_weights[sl], ybuf[p.c_slot_rows[sl] * R + r], acc);
+      }
+      p.out[static_cast<size_t>(t) * H + b * R + r] = float_to_half_bits(acc);
+    }
+  }
+}
+
 // ----------------------------------------------------------------- host -----
 
 // LDS bytes of the A fragments: kXE experts x na rows (stage 2: hi and lo).
@@ -998,6 +1100,17 @@ void set_shared(DecodeArgs& p, int shared_mfma, int T, int top_k, int I, int H) 
 
 // The least LDS a GEMV stage can run with: one A row per pass, one unit per
 // window, plus the routing and cost tables it keeps.
+size_t down_fold_lds(int64_t T, int top_k, int I, int lanes) {
+  const size_t S = static_cast<size_t>(T) * top_k;
+  const size_t b = S * 2 * (I / kGroup) * kFragDwords * 4 + S * (64 / lanes) * 4;
+  return (b + 15) & ~static_cast<size_t>(15);
+}
+
+bool down_fold_ok(int64_t T, int top_k, int I, int lanes, size_t lds_bytes) {
+  return T <= 2 && (I / kGroup) / lanes <= kFoldMaxSpb &&
+         down_fold_lds(T, top_k, I, lanes) + kDecodeStaticLds <= lds_bytes;
+}
+
 size_t gemv_min_lds(bool gate_up, bool route, int64_t T, int top_k, int E, int H, int I,
                     int lanes, bool cost_split) {
   Geom geo{};
@@ -1103,6 +1216,14 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
   p.E = a.E;
   p.y = a.y;
   p.cost_in = ws.tiles;  // written by the gate/up kernel
+  if (a.combine) {  // T <= 2, no shared-expert workgroups (the plan's check)
+    p.c_weights = a.c_weights;
+    p.c_slot_rows = a.c_slot_rows;
+    p.out = a.out;
+    hipLaunchKernelGGL(down_fold_kernel, dim3(static_cast<unsigned>(geo.nb)), dim3(kFoldThreads),
+                       down_fold_lds(a.T, a.top_k, a.I, a.lanes), stream, p, geo);
+    return;
+  }
   set_shared<false>(p, a.shared_mfma, a.T, a.top_k, a.I, a.H);
   launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_per_pass, a.cost_split);
 }

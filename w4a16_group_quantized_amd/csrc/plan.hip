@@ -54,6 +54,9 @@ constexpr int64_t kSharedMfmaMinT = 3;
 // 25.5, 2: 28.7 / 27.7, 4: 33.6 / 32.9, 8: 40.5 / 40.2, 16: 67.6 / 69.0;
 // I = 640: 1 token 30.9 / 30.2, 4: 48.7 / 48.0, 8: 69.2 / 71.8).
 constexpr int64_t kLanes16MaxT = 4;
+// The combine folded into the down GEMV (one workgroup per block of output
+// rows, every active expert) up to this many tokens (its kernel's limit).
+constexpr int64_t kCombineInDownMaxT = 2;
 
 // Lanes per weight row of a GEMV over K = 32 G: the largest power of two
 // <= cap that divides G (a lane takes every lanes-th group of the row).
@@ -95,6 +98,8 @@ Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
   p.rows_per_pass = T >= kRows4MinT ? 4 : (T >= 2 ? 2 : 1);
   p.cost_split = T >= kRows4MinT;
   p.router_gemv = T <= kRouterGemvMaxT && T * static_cast<int64_t>(H) * 2 <= kRouterGemvMaxXBytes;
+  p.combine_in_down = p.ffn == MOE_FFN_GEMV && T <= kCombineInDownMaxT && !p.shared_mfma &&
+                      down_fold_ok(T, kk, I, p.lanes_down, kGfx950LdsBytes);
   // A shared expert of 3 tokens or more whose A rows do not fit in LDS (23
   // and more at H = 2560): the matrix-core FFN, which takes its rows as one
   // more M-tile (block, us, GEMV with the shared expert in it / matrix
@@ -108,6 +113,7 @@ Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
       (shared_no_room || !gemv_fits(p, T, top_k, E, shared, H, I, kGfx950LdsBytes))) {
     p.ffn = MOE_FFN_MFMA;
     p.shared_mfma = 0;
+    p.combine_in_down = 0;
     if (p.route == MOE_ROUTE_IN_GATE_UP)
       p.route = T <= kRouteOneLaunchMaxT && EP <= kRouteOneLaunchMaxE ? MOE_ROUTE_ONE_LAUNCH
                                                                       : MOE_ROUTE_SEPARATE;
@@ -120,12 +126,12 @@ bool gemv_fits(const Plan& p, int64_t T, int top_k, int E, int shared, int H, in
   const int kk = top_k + shared, EP = E + shared;
   const bool route = p.route == MOE_ROUTE_IN_GATE_UP;
   if (p.shared_mfma && shared_mfma_lds(T, H, I) + kDecodeStaticLds > lds_bytes) return false;
+  if (p.combine_in_down && !down_fold_ok(T, kk, I, p.lanes_down, lds_bytes)) return false;
   return gemv_min_lds(true, route, T, kk, EP, H, I, p.lanes_gate_up, p.cost_split) <= lds_bytes &&
          gemv_min_lds(false, false, T, kk, EP, H, I, p.lanes_down, p.cost_split) <= lds_bytes;
 }
 
 int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, int I) {
-  (void)top_k;
   E += shared;
   if (p.ffn != MOE_FFN_GEMV && p.ffn != MOE_FFN_MFMA) return MOE_ERR_INVALID_ARG;
   if (p.rows_per_pass != 1 && p.rows_per_pass != 2 && p.rows_per_pass != 4 &&
@@ -141,6 +147,13 @@ int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, in
     return MOE_ERR_INVALID_ARG;
   if (p.router_gemv != 0 && p.router_gemv != 1) return MOE_ERR_INVALID_ARG;
   if (p.shared_mfma != 0 && p.shared_mfma != 1) return MOE_ERR_INVALID_ARG;
+  if (p.combine_in_down != 0 && p.combine_in_down != 1) return MOE_ERR_INVALID_ARG;
+  // the folded combine: the GEMV, up to 2 tokens, no shared-expert
+  // workgroups, its LDS and steps within the kernel's limits
+  if (p.combine_in_down &&
+      (p.ffn != MOE_FFN_GEMV || p.shared_mfma || !down_fold_ok(T, top_k + shared, I, p.lanes_down,
+                                                                 kGfx950LdsBytes)))
+    return MOE_ERR_UNSUPPORTED;
   if (p.shared_mfma && !shared) return MOE_ERR_INVALID_ARG;
   // the shared expert's matrix-core workgroups: with the GEMV, up to 32 rows
   // (one MFMA tile) whose A rows fit in LDS

@@ -60,7 +60,8 @@ class Plan(ctypes.Structure):
     _fields_ = [("ffn", ctypes.c_int32), ("route", ctypes.c_int32), ("msub", ctypes.c_int32),
                 ("lanes_gate_up", ctypes.c_int32), ("lanes_down", ctypes.c_int32),
                 ("rows_per_pass", ctypes.c_int32), ("cost_split", ctypes.c_int32),
-                ("router_gemv", ctypes.c_int32), ("shared_mfma", ctypes.c_int32)]
+                ("router_gemv", ctypes.c_int32), ("shared_mfma", ctypes.c_int32),
+                ("combine_in_down", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
