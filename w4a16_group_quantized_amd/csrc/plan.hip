@@ -55,7 +55,10 @@ constexpr int64_t kSharedMfmaMinT = 3;
 // I = 640: 1 token 30.9 / 30.2, 4: 48.7 / 48.0, 8: 69.2 / 71.8).
 constexpr int64_t kLanes16MaxT = 4;
 // The combine folded into the down GEMV (one workgroup per block of output
-// rows, every active expert) up to this many tokens (its kernel's limit).
+// rows of every active expert) up to 2 tokens (layer, us, folded / separate
+// combine: I = 160: 1 token 21.4 / 25.1, 2: 26.1 / 27.4; I = 640: 1 token
+// 26.6 / 30.5, 2: 34.3 / 38.1).  A form for up to 4 rows per expert was
+// slower from 3 tokens (4 tokens: I = 160 39.2 / 32.6, I = 640 51.0 / 48.5).
 constexpr int64_t kCombineInDownMaxT = 2;
 
 // Lanes per weight row of a GEMV over K = 32 G: the largest power of two
