@@ -226,6 +226,8 @@ def test_token_counts(dev, T):
     (4, 2, 8192, 64, 4),      # decode, long K of gate/up: 32 steps per row block
     (4, 2, 128, 4096, 3),     # decode, long K of down: 16 steps per row block
     (6, 3, 96, 96, 2),        # decode, odd group counts: one lane per row
+    (4, 4, 128, 128, 2),      # k = E at 2 tokens: every expert holds both rows, S > E
+                              # (the combine inside the down launch)
     (2, 1, 16384, 64, 2),     # largest H, decode GEMV
     (2, 1, 64, 16384, 2),     # largest I at decode size: the down GEMV's A rows do not
                               # fit in LDS, so the matrix-core kernels take it
