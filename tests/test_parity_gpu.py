@@ -449,6 +449,37 @@ def test_gate_up_then_down_equals_grouped_ffn(dev):
     assert torch.equal(y_a, y_b)
 
 
+@pytest.mark.parametrize("T", [1, 8])   # 1: the combine inside the down launch
+def test_graph_replay_of_layer_forward(dev, T):
+    """moe_layer_forward captured in a HIP graph replays to its eager result,
+    with eager work between replays."""
+    from w4a16_group_quantized_amd import ops
+
+    shape = synth.MoEShape(E=64, top_k=6, H=512, I=256, T=T)
+    host = synth.make_inputs(shape, 22)
+    w = ops.weights_to_device(host, dev)
+    logits = torch.from_numpy(host["logits"]).to(dev)
+    x = torch.from_numpy(host["x"]).to(dev)
+    layer = ops.MoELayer(shape.T, shape.E, shape.top_k, shape.H, shape.I, dev)
+    eager = layer.forward(logits, x, w).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            got = layer.forward(logits, x, w)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        got.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {rep}"
+        _ = (got.float() * 2).sum().item()  # eager work between replays
+
+
 @pytest.mark.parametrize("T", [8, 300])
 def test_graph_replay_matches_eager(dev, T):
     """A captured layer call replays to the eager result, with eager work between replays."""

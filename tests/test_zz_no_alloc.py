@@ -49,6 +49,11 @@ def test_noalloc_decode_then_smaller(dev):
     _pair(synth.WORKLOADS["decode_e512_k10_h2560_i640_t8"], 0, dev, 3)   # 3 tokens: 16 lanes per w13 row
 
 
+def test_noalloc_two_tokens_then_one(dev):
+    # up to 2 tokens the combine runs inside the down launch
+    _pair(synth.MoEShape(E=512, top_k=10, H=2560, I=160, T=2), 4, dev, 1)
+
+
 def test_noalloc_prefill_then_smaller(dev):
     _pair(synth.MoEShape(E=64, top_k=6, H=512, I=256, T=200), 3, dev, 90)
 
