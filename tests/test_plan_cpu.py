@@ -99,6 +99,16 @@ def test_rows_per_pass_and_cost_split():
     assert plan(8, E=1023, shared=True)["route"] == ops.ROUTE_IN_GATE_UP
 
 
+def test_combine_inside_down_up_to_two_tokens():
+    assert plan(1)["combine_in_down"] == 1 and plan(2)["combine_in_down"] == 1
+    assert plan(3)["combine_in_down"] == 0 and plan(8)["combine_in_down"] == 0
+    assert plan(1, I=160)["combine_in_down"] == 1
+    assert plan(2, shared=True)["combine_in_down"] == 1   # the shared expert in the GEMV
+    # more than 8 steps per lane (I = 16384 takes the matrix cores anyway) or no LDS room
+    assert plan(1, I=4096)["combine_in_down"] == 0          # 128 groups / 8 lanes = 16 steps
+    assert plan(33)["combine_in_down"] == 0
+
+
 def test_plan_query_rejects_bad_sizes():
     p = ops.Plan()
     lib = ops.load_library()
@@ -136,6 +146,10 @@ def test_layer_rejects_plans_the_sizes_do_not_allow():
     assert _layer(lib, dict(base, rows_per_pass=3)) == ops.MOE_ERR_INVALID_ARG
     assert _layer(lib, dict(base, cost_split=2)) == ops.MOE_ERR_INVALID_ARG
     assert _layer(lib, dict(base, shared_mfma=1)) == ops.MOE_ERR_INVALID_ARG   # no shared expert
+    assert _layer(lib, dict(base, combine_in_down=2)) == ops.MOE_ERR_INVALID_ARG
+    assert _layer(lib, dict(base, combine_in_down=1)) == ops.MOE_ERR_UNSUPPORTED  # 8 tokens
+    assert _layer(lib, dict(plan(2), combine_in_down=1, ffn=ops.FFN_MFMA,
+                            route=ops.ROUTE_ONE_LAUNCH), T=2) == ops.MOE_ERR_UNSUPPORTED
     assert _layer(lib, dict(base, ffn=ops.FFN_MFMA)) == ops.MOE_ERR_UNSUPPORTED  # routing in gate/up
     big = plan(65)
     assert _layer(lib, dict(big, ffn=ops.FFN_GEMV), T=65) == ops.MOE_ERR_UNSUPPORTED
