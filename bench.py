@@ -167,7 +167,8 @@ def kernel_sources(gemv: bool) -> list:
     """Sources whose text fixes the kernels a workload's FFN runs."""
     csrc = "w4a16_group_quantized_amd/csrc/"
     if gemv:
-        return [csrc + "ffn_decode.hip", csrc + "common.h", csrc + "route.h", csrc + "permute.h"]
+        return [csrc + "ffn_decode.hip", csrc + "decode_stage.inc", csrc + "decode_route.inc",
+                csrc + "common.h", csrc + "route.h", csrc + "permute.h"]
     return [csrc + "ffn_prefill.hip", csrc + "common.h"]
 
 
@@ -753,6 +754,9 @@ def candidate_plans(T: int, E: int, k: int, H: int, I: int) -> list:
         if T <= 2:
             for fold in (0, 1):
                 out.append(dict(base, ffn=ops.FFN_GEMV, route=route, combine_in_down=fold))
+        # gate/up and down in one launch, with the default lanes
+        if E <= 1024:
+            out.append(dict(gemv, route=ops.ROUTE_IN_GATE_UP, one_launch=1))
     routes = (ops.ROUTE_ONE_LAUNCH, ops.ROUTE_SEPARATE) if T <= 64 and E <= 1024 else (
         ops.ROUTE_SEPARATE,)
     for msub in (1, 4):

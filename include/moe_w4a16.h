@@ -27,10 +27,12 @@
  *     workspaces.  The library never allocates or frees memory and never
  *     synchronises.  Its only state is a per-device cache of two device
  *     attributes (compute-unit count, LDS bytes per workgroup) read from the
- *     runtime on first use, and the per-device scratch array of
- *     moe_layer_forward_noalloc with its address cache.  Entry points other
- *     than moe_layer_forward_noalloc may be called from several host threads
- *     at once.
+ *     runtime on first use, the per-device scratch array of
+ *     moe_layer_forward_noalloc with its address cache, and the per-device
+ *     completion counts of the one-launch FFN plan (moe_plan.one_launch),
+ *     which every such call leaves at zero.  Entry points other than
+ *     moe_layer_forward_noalloc, and plans other than one_launch, may be
+ *     called from several host threads at once.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *     default stream) and runs asynchronously.  A call that returns MOE_OK has
  *     only enqueued its kernels.
@@ -425,6 +427,14 @@ typedef struct moe_plan {
                              <= 8 and every act row's fragments in LDS), 0 a
                              separate combine launch; the output is the same bit
                              for bit                                                  */
+  int32_t one_launch;     /* GEMV with routing in gate/up, no shared expert, even split
+                             (cost_split = 0), combine_in_down = 0: 1 gate/up and down
+                             in one persistent launch (one workgroup per compute unit;
+                             a workgroup's down share waits, bounded, for the gate/up
+                             units of its experts, on per-device completion counts),
+                             0 two launches; the output is the same bit for bit.
+                             Calls with it that overlap in time on one device share
+                             those counts and must not be issued                      */
 } moe_plan;
 
 /*

@@ -122,14 +122,14 @@ def test_plan_query_rejects_bad_sizes():
     assert lib.moe_plan_default(8, 64, 512, 1, 2560, 640, a) == ops.MOE_ERR_UNSUPPORTED
 
 
-def _layer(lib, d, T=8, E=512, k=10, H=2560, I=640):
+def _layer(lib, d, T=8, E=512, k=10, H=2560, I=640, ws_bytes=1 << 40):
     p = ops.Plan()
     for key, v in d.items():
         setattr(p, key, v)
     ptrs = [FAKE] * 6
     import ctypes
 
-    return lib.moe_layer_forward_plan(FAKE, FAKE, T, E, k, *ptrs, H, I, 32, FAKE, FAKE, 1 << 40,
+    return lib.moe_layer_forward_plan(FAKE, FAKE, T, E, k, *ptrs, H, I, 32, FAKE, FAKE, ws_bytes,
                                       ctypes.addressof(p), None)
 
 
@@ -158,6 +158,50 @@ def test_layer_rejects_plans_the_sizes_do_not_allow():
     assert _layer(lib, dict(plan(8, E=1025), route=ops.ROUTE_IN_GATE_UP), E=1025) == \
         ops.MOE_ERR_UNSUPPORTED
     assert _layer(lib, dict(plan(17), router_gemv=1), T=17) == ops.MOE_ERR_UNSUPPORTED
+
+
+def _block(lib, d, T=8, E=512, k=10, H=2560, I=640, shared=1):
+    p = ops.Plan()
+    for key, v in d.items():
+        setattr(p, key, v)
+    import ctypes
+
+    return lib.moe_block_forward_plan(FAKE, T, FAKE, E, k, shared, *([FAKE] * 6), H, I, 32, FAKE,
+                                      FAKE, FAKE, 1 << 40, ctypes.addressof(p), None)
+
+
+def test_one_launch_ffn_limits():
+    """The one-launch FFN is never a default (slower than two launches at every
+    size swept) and is accepted only with the GEMV routing inside gate/up, no
+    shared expert, an even split and a separate combine."""
+    for T in (1, 2, 8, 9, 16, 32, 64, 1024):
+        assert plan(T)["one_launch"] == 0
+        assert plan(T, I=160, shared=True)["one_launch"] == 0
+    lib = ops.load_library()
+    base = dict(plan(8), cost_split=0)
+    assert _layer(lib, dict(base, one_launch=2)) == ops.MOE_ERR_INVALID_ARG
+    assert _layer(lib, dict(base, one_launch=-1)) == ops.MOE_ERR_INVALID_ARG
+    assert _layer(lib, dict(base, one_launch=1, cost_split=1)) == ops.MOE_ERR_UNSUPPORTED
+    assert _layer(lib, dict(base, one_launch=1, route=ops.ROUTE_ONE_LAUNCH)) == \
+        ops.MOE_ERR_UNSUPPORTED
+    assert _layer(lib, dict(base, one_launch=1, route=ops.ROUTE_SEPARATE)) == ops.MOE_ERR_UNSUPPORTED
+    assert _layer(lib, dict(base, one_launch=1, ffn=ops.FFN_MFMA, route=ops.ROUTE_SEPARATE)) == \
+        ops.MOE_ERR_UNSUPPORTED
+    assert _layer(lib, dict(plan(1), one_launch=1), T=1) == ops.MOE_ERR_UNSUPPORTED  # folded combine
+    assert _layer(lib, dict(plan(65), ffn=ops.FFN_GEMV, route=ops.ROUTE_IN_GATE_UP,
+                            one_launch=1), T=65) == ops.MOE_ERR_UNSUPPORTED
+    # the block with its shared expert
+    blk = dict(plan(8, shared=True), shared_mfma=0, cost_split=0, one_launch=1)
+    assert _block(lib, blk) == ops.MOE_ERR_UNSUPPORTED
+    # both stages' LDS (a plan that passes stops at the 1-byte workspace, before
+    # anything is enqueued): at I = 15360 the down stage's fragments fit beside
+    # the routing tables of 8 experts, not beside those of 1024
+    for E, ok in ((8, True), (1024, False)):
+        two = dict(plan(8, E=E, k=2, H=256, I=15360), cost_split=0)
+        assert two["ffn"] == ops.FFN_GEMV and two["route"] == ops.ROUTE_IN_GATE_UP
+        assert _layer(lib, two, T=8, E=E, k=2, H=256, I=15360, ws_bytes=1) == ops.MOE_ERR_WORKSPACE
+        assert _layer(lib, dict(two, one_launch=1), T=8, E=E, k=2, H=256, I=15360, ws_bytes=1) == \
+            (ops.MOE_ERR_WORKSPACE if ok else ops.MOE_ERR_UNSUPPORTED)
 
 
 def test_gemv_that_does_not_fit_lds_falls_back_or_is_refused():

@@ -517,6 +517,17 @@ static int layer_run(const float* logits, const uint16_t* x, int64_t T, int32_t 
   d.sc = w2_scales;
   d.qz = w2_qzeros;
   d.y = w.y;
+  if (pl.one_launch) {
+    // routing, gate/up and down in one launch, then the combine
+    const FfnWorkspace fws = ffn_workspace_carve(w.ffn, T, kk, EP, H, I);
+    a.lanes = pl.lanes_gate_up;
+    a.rows_per_pass = pl.rows_per_pass;
+    d.lanes = pl.lanes_down;
+    const RouteOut r{w.ids, w.weights, w.offsets, w.sorted, w.slot_rows, w.active, w.num_active};
+    launch_one_launch_decode(logits, a, d, r, fws, st);
+    launch_combine(w.y, w.weights, w.slot_rows, static_cast<int>(T), kk, H, out, st);
+    return check_launch();
+  }
   if (pl.route == MOE_ROUTE_IN_GATE_UP) {
     // the gate/up GEMV routes the tokens itself
     const FfnWorkspace fws = ffn_workspace_carve(w.ffn, T, kk, EP, H, I);

@@ -133,6 +133,11 @@ struct RouteOut {
 void launch_route_gate_up_decode(const float* logits, const GateUpArgs& a, const RouteOut& r,
                                  const FfnWorkspace& ws, hipStream_t stream);
 void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t stream);
+// Gate/up (routing inside) and down in one persistent launch; a.lanes and
+// d.lanes are the two stages' lanes per row, a.rows_per_pass the A rows per
+// pass; no shared expert, even split.
+void launch_one_launch_decode(const float* logits, const GateUpArgs& a, const DownArgs& d,
+                              const RouteOut& r, const FfnWorkspace& ws, hipStream_t stream);
 
 // Least LDS bytes one workgroup of a GEMV stage needs at these sizes and
 // lanes per row (ffn_decode.hip); a plan whose GEMV needs more than the
@@ -144,6 +149,10 @@ size_t gemv_min_lds(bool gate_up, bool route, int64_t T, int top_k, int E, int H
 // (at most 8 steps per lane, LDS within lds_bytes).
 size_t down_fold_lds(int64_t T, int top_k, int I, int lanes);
 bool down_fold_ok(int64_t T, int top_k, int I, int lanes, size_t lds_bytes);
+// Least LDS bytes of the one-launch FFN's workgroup (routing tables and the
+// larger stage).
+size_t one_launch_min_lds(int64_t T, int top_k, int E, int H, int I, int lanes_gate_up,
+                          int lanes_down);
 // LDS of the shared expert's matrix-core workgroups inside the GEMV launches
 // (A rows of both stages and the K-split partial sums), T <= 32.
 size_t shared_mfma_lds(int64_t T, int H, int I);

@@ -557,6 +557,51 @@ __device__ __forceinline__ void shared_expert_mfma(const DecodeArgs& p, uint32_t
   }
 }
 
+// Polls a stage-1 completion count (agent scope) until it reaches `target`.
+// Bounded: it gives up after kWaitTicks of the 100 MHz real-time counter and
+// returns false (the caller then writes NaN), so a wait never hangs.
+constexpr uint64_t kWaitTicks = 20000000;  // 200 ms
+__device__ __forceinline__ bool wait_count(const int* ctr, int target) {
+  int* c = const_cast<int*>(ctr);
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return true;
+}
+
+// One stage of the one-launch FFN over this workgroup's share of the units,
+// with the routing tables in LDS (ract, roff, rsorted); `area` holds the
+// stage's LDS areas (frag_bytes, then wmax unit slots).  The stage body is
+// decode_kernel's (decode_stage.inc).  WAIT (stage 2): a window's act rows
+// are staged only once every stage-1 unit of its experts is done (done[a]
+// reaches `target` for each of its active slots a); a wait that runs out
+// (wait_count) makes the window write NaN instead of y.
+template <bool GATE_UP, int NA, bool WAIT>
+__device__ __forceinline__ void one_launch_stage(const DecodeArgs& p, const Geom& geo,
+                                                 uint32_t* area, int& queue, int& poison,
+                                                 const int* ract, const int* roff,
+                                                 const int* rsorted, int n_active,
+                                                 const int* done, int target) {
+  constexpr int FPR = GATE_UP ? 1 : 2;        // fragments per A row (stage 2: hi, lo)
+  constexpr int NF = NA * FPR;                // fragments per expert and pass
+  const int G = geo.G, C = geo.C, spb = geo.spb, nb = geo.nb;
+  const int I = p.I, H = p.H;
+  const int rows_w = GATE_UP ? 2 * I : H;
+  const int R = 64 / C, half = R >> 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k = lane / C, lc = lane & (C - 1);
+  uint32_t* frags = area;
+  uint16_t* scales = reinterpret_cast<uint16_t*>(area + kXE * NF * G * kFragDwords);
+  int* ucost = reinterpret_cast<int*>(scales + geo.wmax * unit_scale_halves(spb));
+  auto active_at = [&](int a) { return ract[a]; };
+  auto offset_at = [&](int e) { return roff[e]; };
+  auto sorted_at = [&](int r) { return rsorted[r]; };
+#include "decode_stage.inc"
+}
+
 // NPL > 0 (stage 1 only): the workgroup first routes the tokens itself, with
 // the router's and permutation's own steps (route.h, permute.h), from
 // logits of E <= 64 NPL experts; workgroup 0 writes the routing out.  Every
@@ -592,61 +637,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   int* rsorted = nullptr;
   int n_active;
   if constexpr (NPL > 0) {
-    const int E = p.E, S = p.T * p.top_k;
-    const int tid = threadIdx.x;
-    auto* rmask = reinterpret_cast<unsigned long long*>(ucost + geo.ucap);
-    roff = reinterpret_cast<int*>(rmask + E);
-    ract = roff + E + 1;
-    rsorted = ract + E;
-    int* rslot = rsorted + S;
-    int* rnum = rslot + S;
-    int* wtot = rnum + 1;
-    for (int e = tid; e < E; e += kThreads) rmask[e] = 0ull;
-    __syncthreads();
-    const int El = E - p.shared, kr = p.top_k - p.shared;  // logits columns, routed choices
-    for (int t = wave; t < p.T; t += kWaves) {
-      int id;
-      float logit, top;
-      wave_topk<NPL>(p.logits + static_cast<size_t>(t) * El, El, kr, id, logit, top);
-      const float w = wave_topk_weight(logit, top, kr);
-      if (lane < p.top_k) {
-        const bool sh = lane == kr;  // only when shared
-        const int sl = t * p.top_k + lane;
-        const int e = sh ? El : id;
-        rslot[sl] = e;
-        atomicOr(&rmask[e], 1ull << t);
-        if (blockIdx.x == 0) {
-          p.r_ids[sl] = e;
-          p.r_weights[sl] = sh ? 1.f : w;
-        }
-      }
-    }
-    __syncthreads();
-    int cnt[kPerThread], off[kPerThread];
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int e = kPerThread * tid + i;
-      cnt[i] = (e < E) ? __popcll(rmask[e]) : 0;
-    }
-    write_offsets_and_active(cnt, E, S, roff, ract, rnum, wtot, off);
-    __syncthreads();
-    for (int sl = tid; sl < S; sl += kThreads) {
-      const int t = sl / p.top_k;
-      const int e = rslot[sl];
-      const int r = roff[e] + __popcll(rmask[e] & ((1ull << t) - 1ull));
-      rsorted[r] = sl;
-      if (blockIdx.x == 0) {
-        p.r_sorted[r] = sl;
-        p.r_slot_rows[sl] = r;
-      }
-    }
-    if (blockIdx.x == 0) {
-      for (int e = tid; e <= E; e += kThreads) p.r_offsets[e] = roff[e];
-      for (int e = tid; e < E; e += kThreads) p.r_active[e] = ract[e];
-      if (tid == 0) *p.r_num_active = *rnum;
-    }
-    __syncthreads();
-    n_active = *rnum;
+    void* const rbase = ucost + geo.ucap;  // the routing tables, past the cost table
+#include "decode_route.inc"
   } else {
     n_active = *p.num_active;
   }
@@ -656,247 +648,81 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs p, Geom geo
   auto offset_at = [&](int e) { if constexpr (NPL > 0) return roff[e]; else return p.offsets[e]; };
   auto sorted_at = [&](int r) { if constexpr (NPL > 0) return rsorted[r]; else return p.sorted_slots[r]; };
 
-  int u0, u1;  // this workgroup's units
-  if (!geo.weighted) {
-    // in 32 bits when the products fit (a 64-bit division is a long
-    // instruction sequence that every wave runs before its first load)
-    const uint64_t U = static_cast<uint64_t>(n_active) * nb;
-    if (U * geo.nwg < (1ull << 32)) {
-      const uint32_t U32 = static_cast<uint32_t>(U);
-      u0 = static_cast<int>(U32 * blockIdx.x / static_cast<uint32_t>(geo.nwg));
-      u1 = static_cast<int>(U32 * (blockIdx.x + 1) / static_cast<uint32_t>(geo.nwg));
-    } else {
-      u0 = static_cast<int>(U * blockIdx.x / geo.nwg);
-      u1 = static_cast<int>(U * (blockIdx.x + 1) / geo.nwg);
-    }
-  } else {
-    // Per-unit cost prefix of the active experts (see the units section):
-    // computed by the gate/up kernel, read back by the down kernel.
-    const int n_cost = n_active;
-    if constexpr (GATE_UP) {
-      const int a = threadIdx.x;  // n_active <= kThreads (E <= 1024 here, or S <= 512)
-      int c = 0;
-      if (a < n_cost) {
-        const int e = active_at(a);
-        c = unit_cost(offset_at(e + 1) - offset_at(e), NA);
-      }
-      int total;
-      const int ex = block_exclusive_scan(c, ucost + geo.ucap - (kScanThreads / 64 + 1), total);
-      if (a < n_cost) ucost[a] = ex;
-      if (a == 0) ucost[n_cost] = total;
-      if (blockIdx.x == 0 && a <= n_cost) p.cost_out[a] = a < n_cost ? ex : total;
-    } else {
-      for (int a = threadIdx.x; a <= n_cost; a += kThreads) ucost[a] = p.cost_in[a];
-    }
-    __syncthreads();
-    // the units that start in this workgroup's share of the cost
-    const int64_t ctot = static_cast<int64_t>(nb) * ucost[n_cost];
-    u0 = first_unit(ucost, n_cost, nb, ctot * blockIdx.x / geo.nwg);
-    u1 = first_unit(ucost, n_cost, nb, ctot * (blockIdx.x + 1) / geo.nwg);
+  // a kernel of its own never waits (the body's WAIT code compiles away)
+  constexpr bool WAIT = false;
+  const int* const done = nullptr;
+  const int target = 0;
+  int& poison = queue;
+#include "decode_stage.inc"
+}
+
+// Completion counts of the one-launch FFN, per device: [a] the stage-1 units
+// done of active slot a, [kOneLaunchMaxSlots] the workgroups that have
+// finished.  Zero at module load; the last workgroup of every launch sets
+// them back to zero.
+constexpr int kOneLaunchMaxSlots = 1024;
+__device__ int g_one_launch_sync[kOneLaunchMaxSlots + 1];
+
+// Gate/up and down in one persistent launch (routing inside, T <= 64 tokens,
+// E <= 1024 experts), one workgroup per compute unit.  Every workgroup routes
+// the tokens (decode_route.inc) and runs its stage-1 share; once its act stores
+// have completed it publishes, after an agent-scope release, how many stage-1
+// units of each active expert it did, and runs its stage-2 share, whose
+// windows issue their weight loads at once and stage their act rows once the
+// experts' counts are complete (after an agent-scope acquire).  Stage 1 never
+// waits, so with every workgroup resident every wait ends; a wait that runs
+// out (another kernel holding compute units for 200 ms) makes its window
+// write NaN.  The shares, units and arithmetic are those of the two separate
+// kernels with an even split, so the results are theirs bit for bit.  Calls
+// that overlap in time on one device share the counts and must not be issued.
+template <int NA, int NPL>
+__global__ __launch_bounds__(kThreads) void one_launch_kernel(DecodeArgs p1, Geom g1, DecodeArgs p2,
+                                                              Geom g2, int table_bytes) {
+  extern __shared__ __align__(16) uint32_t lds[];
+  __shared__ int queue;
+  __shared__ int poison;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int* ract = nullptr;     // LDS: active list, offsets, sorted slots
+  int* roff = nullptr;
+  int* rsorted = nullptr;
+  int n_active;
+  {
+    const DecodeArgs& p = p1;
+    void* const rbase = lds;  // the routing tables, at the start of LDS
+#include "decode_route.inc"
   }
+  uint32_t* area = lds + table_bytes / 4;  // each stage's fragments and unit slots, in turn
+  int* sync = g_one_launch_sync;
 
-  for (int w0 = u0; w0 < u1;) {
-    const int a0 = w0 / nb;
-    const int w1 = min(u1, min(w0 + geo.wmax, (a0 + kXE) * nb));
-    const int nx = (w1 - 1) / nb - a0 + 1;
-    // the window's experts; their row counts are read once the weight loads
-    // of the first pass are out (that pass needs none: every active expert
-    // has a row)
-    int xe[kXE], xr0[kXE] = {0, 0}, xrows[kXE] = {1, 1};
-    // both entries loaded together (a clamped index instead of a branch per
-    // entry, which waited for each load in turn)
-#pragma unroll
-    for (int i = 0; i < kXE; ++i) xe[i] = active_at(min(a0 + i, n_active - 1));
-    __builtin_amdgcn_sched_barrier(0);  // both loads issued before either is used
-#pragma unroll
-    for (int i = 0; i < kXE; ++i) xe[i] = i < nx ? xe[i] : 0;
-    int maxrows = 1;
-    for (int c = 0; c < maxrows; c += NA) {
-      if (w0 != u0 || c != 0) lds_barrier();  // the previous pass no longer reads LDS
-      auto has_rows = [&](int u) { return c == 0 || pick(xrows, u / nb - a0) > c; };
-      auto take = [&]() -> int {  // next unit from the window's counter, or -1
-        int u;
-        do {
-          int t = 0;
-          if (lane == 0) t = atomicAdd(&queue, 1);
-          u = __builtin_amdgcn_readfirstlane(t);
-        } while (u < w1 && !has_rows(u));
-        return u < w1 ? u : -1;
-      };
-      // ---- load side.  lu is the unit being loaded, -2 when the next one is
-      // still to be taken from the counter, -1 when the window is done.  The
-      // ring is primed with the wave's first unit (unit w0 + wave) before
-      // staging; the counter is only used once staging is over.
-      Slot ring[kDepth];
-      int su[kDepth], sj[kDepth];  // unit (-1: none) and step of each ring slot
-      int lu = (w0 + wave < w1 && has_rows(w0 + wave)) ? w0 + wave : -2;
-      int lj = 0;
-      ExpertBufs lbufs = expert_bufs(p, rows_w, G, xe[0]);
-      uint32_t lrow = rows_w;
-      // A unit's scales are loaded when the load side enters it (held in sc0,
-      // sc1) and written to the unit's LDS slot when the compute side starts
-      // it; with the registers still holding a unit not yet written, the load
-      // side waits (only when a unit has fewer steps than the ring has slots).
-      // Units with more than kMaxSpbHeld steps are copied synchronously by
-      // the compute side instead.
-      const int nch = 8 * spb;
-      const bool held = spb <= kMaxSpbHeld;
-      uint4 sc0 = make_uint4(0, 0, 0, 0), sc1 = sc0;
-      bool pending = false;
-      auto issue = [&](int d, bool may_take) {
-        if (lu == -2 && may_take) lu = take();
-        const bool on = lu >= 0 && !(lj == 0 && pending);
-        if (on && lj == 0) {  // entering unit lu
-          const int a = lu / nb;
-          const int b = lu - a * nb;
-          lbufs = expert_bufs(p, rows_w, G, pick(xe, a - a0));
-          lrow = static_cast<uint32_t>(block_row<GATE_UP>(b, k, R, I, H));
-          if (held) {
-            sc0 = load_b128(lbufs.s, scale_chunk<GATE_UP>(I, G, spb, R, b, min(lane, nch - 1)));
-            sc1 = load_b128(lbufs.s, scale_chunk<GATE_UP>(I, G, spb, R, b, min(lane + 64, nch - 1)));
-            pending = true;
-          }
-        }
-        issue_step(lbufs, G, on ? lrow : rows_w, lj * C + lc, ring[d]);
-        su[d] = on ? lu : -1;
-        sj[d] = lj;
-        if (on && ++lj == spb) {
-          lj = 0;
-          lu = -2;
-        }
-      };
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) issue(d, false);
-
-      if (c == 0) {
-#pragma unroll
-        for (int i = 0; i < kXE; ++i) {
-          xr0[i] = i < nx ? offset_at(xe[i]) : 0;
-          xrows[i] = i < nx ? offset_at(xe[i] + 1) - xr0[i] : 0;
-          maxrows = max(maxrows, xrows[i]);
-        }
-      }
-      // this pass's A rows
-      for (int i = threadIdx.x; i < kXE * NF * G; i += kThreads) {
-        const int xi = i / (NF * G);
-        const int rem = i - xi * (NF * G);
-        const int f = rem / G;
-        const int g = rem - f * G;
-        const int m = c + f / FPR;
-        if (xi < nx && m < pick(xrows, xi)) {
-          const int r = pick(xr0, xi) + m;
-          const uint16_t* src;
-          if (GATE_UP) {
-            src = p.x + static_cast<size_t>(sorted_at(r) / p.top_k) * H;
-          } else {
-            src = ((f & 1) ? p.a_lo : p.a_hi) + static_cast<size_t>(r) * I;
-          }
-          stage_frag(src + 32 * g, frags + i * kFragDwords);
-        }
-      }
-      if (threadIdx.x == 0) queue = w0 + kWaves;
-      lds_barrier();
-
-      // compute side: one accumulator per A row (stage 2 adds the row's hi
-      // and lo group dots, each unbiased on its own, before scaling)
-      float acc[NA];
-#pragma unroll
-      for (int m = 0; m < NA; ++m) acc[m] = 0.f;
-      int cmc = 0, crf = 0, cscale = 0;
-      int fb[NA];  // LDS dword offset of each A row's first fragment
-#pragma unroll
-      for (int m = 0; m < NA; ++m) fb[m] = 0;
-      uint32_t crow = 0;
-      int cb = 0;
-      bool live = true;
-      while (live) {
-        live = lu != -1;
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-          if (su[d] >= 0) {
-            live = true;
-            const int j = sj[d];
-            if (j == 0) {  // a new unit: its expert, block and staged data
-              const int u = su[d];
-              const int a = u / nb;
-              const int xi = a - a0;
-              cb = u - a * nb;
-              crow = static_cast<uint32_t>(block_row<GATE_UP>(cb, k, R, I, H));
-              cmc = min(NA, pick(xrows, xi) - c);
-              crf = pick(xr0, xi) + c;
-#pragma unroll
-              for (int m = 0; m < NA; ++m) fb[m] = (xi * NF + m * FPR) * G * kFragDwords;
-              uint4* slot4 = reinterpret_cast<uint4*>(scales + (u - w0) * unit_scale_halves(spb));
-              if (held) {  // chunks lane and lane + 64 (repeats of the last one past the end)
-                slot4[min(lane, nch - 1)] = sc0;
-                slot4[min(lane + 64, nch - 1)] = sc1;
-                pending = false;
-              } else {
-                const ExpertBufs cb_bufs = expert_bufs(p, rows_w, G, pick(xe, xi));
-                for (int i = lane; i < nch; i += 64)
-                  slot4[i] = load_b128(cb_bufs.s, scale_chunk<GATE_UP>(I, G, spb, R, cb, i));
-              }
-              cscale = (u - w0) * unit_scale_halves(spb) +
-                       (GATE_UP ? (k < half ? 0 : 32 * spb) + (k < half ? k : k - half) * G : k * G);
-            }
-            const int gg = j * C + lc;
-            // LDS reads first: they do not wait for the weight loads.  Every
-            // chunk has at least one A row, so row 0's fragments are in use.
-            Frag fp[FPR];
-#pragma unroll
-            for (int f = 0; f < FPR; ++f) fp[f] = read_frag(frags + fb[0] + (f * G + gg) * kFragDwords);
-            const float scale = half_bits_to_float(scales[cscale + gg]);
-            __builtin_amdgcn_sched_barrier(0);
-            const Slot& sl = ring[d];
-            const float z = static_cast<float>((sl.zw >> (4u * (crow & 7u))) & 0xFu);
-            const Codes codes = expand_codes(sl.q);
-            {
-              float dsum = group_dot(codes, z, fp[0]);
-              if (FPR == 2) dsum += group_dot(codes, z, fp[FPR - 1]);
-              acc[0] = fmaf(scale, dsum, acc[0]);
-            }
-#pragma unroll
-            for (int m = 1; m < NA; ++m)
-              if (m < cmc) {
-                float dsum = group_dot(codes, z, read_frag(frags + fb[m] + gg * kFragDwords));
-                if (FPR == 2)
-                  dsum += group_dot(codes, z, read_frag(frags + fb[m] + (G + gg) * kFragDwords));
-                acc[m] = fmaf(scale, dsum, acc[m]);
-              }
-            if (j == spb - 1) {  // block done: finish its rows
-#pragma unroll
-              for (int m = 0; m < NA; ++m) {
-                if (m < cmc) {
-                  if (GATE_UP) {
-                    const float v = cluster_sum(acc[m], C);
-                    const float up = __shfl_xor(v, 32, 64);  // up half of the wave -> gate half
-                    const int col = cb * half + k;
-                    if (lane < 32 && lc == 0 && col < I) {
-                      const float act = v / (1.f + expf(-v)) * up;
-                      const uint16_t hi = float_to_half_bits(act);
-                      const uint16_t lo = float_to_half_bits(act - half_bits_to_float(hi));
-                      const size_t idx = static_cast<size_t>(crf + m) * I + col;
-                      p.act_hi[idx] = hi;
-                      p.act_lo[idx] = lo;
-                    }
-                  } else {
-                    const float v = cluster_sum(acc[m], C);
-                    const int n = cb * R + k;
-                    if (lc == 0 && n < H) p.y[static_cast<size_t>(crf + m) * H + n] = v;
-                  }
-                }
-              }
-#pragma unroll
-              for (int m = 0; m < NA; ++m) acc[m] = 0.f;
-            }
-          }
-          // Refill this slot with the next step; once the window is done this
-          // is a no-load, issued anyway so every path keeps the same counts.
-          issue(d, true);
-        }
-      }
+  one_launch_stage<true, NA, false>(p1, g1, area, queue, poison, ract, roff, rsorted, n_active,
+                                    nullptr, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's act stores have completed
+  __syncthreads();                // (and no wave reads stage 1's LDS areas any more)
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // this workgroup's stage-1 share, as the stage body splits the units evenly
+    const int nb = g1.nb;
+    const int64_t U = static_cast<int64_t>(n_active) * nb;
+    const int u0 = static_cast<int>(U * blockIdx.x / g1.nwg);
+    const int u1 = static_cast<int>(U * (blockIdx.x + 1) / g1.nwg);
+    for (int a = u0 / nb; a < n_active && a * nb < u1; ++a) {
+      const int c = min(u1, (a + 1) * nb) - max(u0, a * nb);
+      if (c > 0) __hip_atomic_fetch_add(sync + a, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    w0 = w1;
+  }
+  one_launch_stage<false, NA, true>(p2, g2, area, queue, poison, ract, roff, rsorted, n_active,
+                                    sync, g1.nb);
+
+  // the last workgroup out (every other one is past its waits) resets the counts
+  __syncthreads();
+  if (threadIdx.x == 0)
+    poison = __hip_atomic_fetch_add(sync + kOneLaunchMaxSlots, 1, __ATOMIC_ACQ_REL,
+                                    __HIP_MEMORY_SCOPE_AGENT) == static_cast<int>(gridDim.x) - 1;
+  __syncthreads();
+  if (poison) {
+    for (int a = threadIdx.x; a <= kOneLaunchMaxSlots; a += kThreads)
+      __hip_atomic_store(sync + a, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1009,19 +835,36 @@ size_t frag_bytes(const Geom& geo, int na) {
 // size, from the LDS a workgroup may hold.  Windows aim to cover a
 // workgroup's whole share of units, which is at most ceil(slots * nb / nwg).
 template <bool GATE_UP>
+struct WindowBudget {
+  size_t budget;  // LDS bytes for fragments and unit slots
+  size_t unit;    // bytes of one unit slot
+  int want;       // units of the largest share, plus one
+  WindowBudget(const Geom& geo, int slots, const DeviceInfo& dev, size_t reserved)
+      : budget(static_cast<size_t>(dev.lds) - kDecodeStaticLds - reserved),
+        unit(static_cast<size_t>(unit_scale_halves(geo.spb)) * 2),
+        want(static_cast<int>((static_cast<int64_t>(slots) * geo.nb + geo.nwg - 1) / geo.nwg) + 1) {}
+  // na rows per pass leave room for a useful window
+  bool roomy(const Geom& geo, int na) const {
+    return frag_bytes<GATE_UP>(geo, na) + unit * min(want, 16) <= budget;
+  }
+  // the window size that fills the rest of the budget
+  void set_wmax(Geom& geo, int na) const {
+    const size_t fb = frag_bytes<GATE_UP>(geo, na);
+    const size_t rest = budget > fb ? budget - fb : 0;
+    size_t w = rest / unit;
+    if (w > static_cast<size_t>(want)) w = want;
+    geo.wmax = w < 1 ? 1 : static_cast<int>(w);
+  }
+};
+
+template <bool GATE_UP>
 int plan(Geom& geo, int slots, const DeviceInfo& dev, size_t reserved, int rows_per_pass) {
-  const size_t budget = static_cast<size_t>(dev.lds) - kDecodeStaticLds - reserved;
-  const size_t unit = static_cast<size_t>(unit_scale_halves(geo.spb)) * 2;
-  const int want = static_cast<int>((static_cast<int64_t>(slots) * geo.nb + geo.nwg - 1) / geo.nwg) + 1;
+  const WindowBudget<GATE_UP> wb(geo, slots, dev, reserved);
   // the plan's rows per pass; stage 2 stops at 4 (eight rows of hi and lo
   // fragments would spill registers), and fewer when LDS is short
   int na = GATE_UP ? rows_per_pass : min(rows_per_pass, 4);
-  while (na > 1 && frag_bytes<GATE_UP>(geo, na) + unit * min(want, 16) > budget) na /= 2;
-  const size_t fb = frag_bytes<GATE_UP>(geo, na);
-  const size_t rest = budget > fb ? budget - fb : 0;
-  size_t w = rest / unit;
-  if (w > static_cast<size_t>(want)) w = want;
-  geo.wmax = w < 1 ? 1 : static_cast<int>(w);
+  while (na > 1 && !wb.roomy(geo, na)) na /= 2;
+  wb.set_wmax(geo, na);
   return na;
 }
 
@@ -1226,6 +1069,91 @@ void launch_down_decode(const DownArgs& a, const FfnWorkspace& ws, hipStream_t s
   }
   set_shared<false>(p, a.shared_mfma, a.T, a.top_k, a.I, a.H);
   launch_decode<false>(p, geo, min(a.E, a.T * a.top_k), stream, false, a.rows_per_pass, a.cost_split);
+}
+
+// Gate/up and down in one launch (one_launch_kernel): the two stages'
+// geometry as the separate launches set it, even split, no shared-expert
+// workgroups; both stages take the same rows per pass (the largest <= 4 that
+// leaves both of them a useful window), each its own window size.
+void launch_one_launch_decode(const float* logits, const GateUpArgs& a, const DownArgs& d,
+                              const RouteOut& r, const FfnWorkspace& ws, hipStream_t stream) {
+  const DeviceInfo dev = device_info();
+  Geom g1{}, g2{};
+  g1.G = a.H / kGroup;
+  g1.C = a.lanes;
+  g1.spb = g1.G / g1.C;
+  g1.nb = (a.I + (64 / g1.C) / 2 - 1) / ((64 / g1.C) / 2);
+  g2.G = a.I / kGroup;
+  g2.C = d.lanes;
+  g2.spb = g2.G / g2.C;
+  g2.nb = (a.H + 64 / g2.C - 1) / (64 / g2.C);
+  g1.nwg = g2.nwg = dev.cus;
+  DecodeArgs p1{};
+  p1.x = a.x;
+  p1.qw = a.qw;
+  p1.sc = a.sc;
+  p1.qz = a.qz;
+  p1.T = a.T;
+  p1.top_k = a.top_k;
+  p1.H = a.H;
+  p1.I = a.I;
+  p1.E = a.E;
+  p1.act_hi = ws.act_hi;
+  p1.act_lo = ws.act_lo;
+  p1.logits = logits;
+  p1.r_ids = r.ids;
+  p1.r_weights = r.weights;
+  p1.r_offsets = r.offsets;
+  p1.r_sorted = r.sorted_slots;
+  p1.r_slot_rows = r.slot_rows;
+  p1.r_active = r.active;
+  p1.r_num_active = r.num_active;
+  DecodeArgs p2{};
+  p2.a_hi = ws.act_hi;
+  p2.a_lo = ws.act_lo;
+  p2.qw = d.qw;
+  p2.sc = d.sc;
+  p2.qz = d.qz;
+  p2.T = d.T;
+  p2.top_k = d.top_k;
+  p2.H = d.H;
+  p2.I = d.I;
+  p2.E = d.E;
+  p2.y = d.y;
+  const int slots = min(a.E, a.T * a.top_k);
+  const size_t rbytes = route_lds_bytes(a.E, a.T * a.top_k);
+  const WindowBudget<true> b1(g1, slots, dev, rbytes);
+  const WindowBudget<false> b2(g2, slots, dev, rbytes);
+  int na = min(a.rows_per_pass, 4);
+  while (na > 1 && !(b1.roomy(g1, na) && b2.roomy(g2, na))) na /= 2;
+  b1.set_wmax(g1, na);
+  b2.set_wmax(g2, na);
+  const size_t lds = rbytes + std::max(launch_lds<true>(g1, na), launch_lds<false>(g2, na));
+  const dim3 grid(static_cast<unsigned>(dev.cus)), block(kThreads);
+  const int tb = static_cast<int>(rbytes);
+  if (a.E <= 512) {
+    if (na == 4)
+      hipLaunchKernelGGL((one_launch_kernel<4, 8>), grid, block, lds, stream, p1, g1, p2, g2, tb);
+    else if (na == 2)
+      hipLaunchKernelGGL((one_launch_kernel<2, 8>), grid, block, lds, stream, p1, g1, p2, g2, tb);
+    else
+      hipLaunchKernelGGL((one_launch_kernel<1, 8>), grid, block, lds, stream, p1, g1, p2, g2, tb);
+  } else {
+    if (na == 4)
+      hipLaunchKernelGGL((one_launch_kernel<4, 16>), grid, block, lds, stream, p1, g1, p2, g2, tb);
+    else if (na == 2)
+      hipLaunchKernelGGL((one_launch_kernel<2, 16>), grid, block, lds, stream, p1, g1, p2, g2, tb);
+    else
+      hipLaunchKernelGGL((one_launch_kernel<1, 16>), grid, block, lds, stream, p1, g1, p2, g2, tb);
+  }
+}
+
+// The least LDS the one-launch FFN runs with: the routing tables and the
+// larger of the two stages at one A row per pass and one unit per window.
+size_t one_launch_min_lds(int64_t T, int top_k, int E, int H, int I, int lanes_gate_up,
+                          int lanes_down) {
+  return std::max(gemv_min_lds(true, true, T, top_k, E, H, I, lanes_gate_up, false),
+                  gemv_min_lds(false, true, T, top_k, E, H, I, lanes_down, false));
 }
 
 }  // namespace moe

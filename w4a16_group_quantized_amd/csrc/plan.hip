@@ -101,6 +101,8 @@ Plan default_plan(int64_t T, int top_k, int E, int shared, int H, int I) {
   p.rows_per_pass = T >= kRows4MinT ? 4 : (T >= 2 ? 2 : 1);
   p.cost_split = T >= kRows4MinT;
   p.router_gemv = T <= kRouterGemvMaxT && T * static_cast<int64_t>(H) * 2 <= kRouterGemvMaxXBytes;
+  // the one-launch FFN is slower than two launches at every size swept
+  p.one_launch = 0;
   p.combine_in_down = p.ffn == MOE_FFN_GEMV && T <= kCombineInDownMaxT && !p.shared_mfma &&
                       down_fold_ok(T, kk, I, p.lanes_down, kGfx950LdsBytes);
   // A shared expert of 3 tokens or more whose A rows do not fit in LDS (23
@@ -130,6 +132,9 @@ bool gemv_fits(const Plan& p, int64_t T, int top_k, int E, int shared, int H, in
   const bool route = p.route == MOE_ROUTE_IN_GATE_UP;
   if (p.shared_mfma && shared_mfma_lds(T, H, I) + kDecodeStaticLds > lds_bytes) return false;
   if (p.combine_in_down && !down_fold_ok(T, kk, I, p.lanes_down, lds_bytes)) return false;
+  if (p.one_launch &&
+      one_launch_min_lds(T, kk, EP, H, I, p.lanes_gate_up, p.lanes_down) > lds_bytes)
+    return false;
   return gemv_min_lds(true, route, T, kk, EP, H, I, p.lanes_gate_up, p.cost_split) <= lds_bytes &&
          gemv_min_lds(false, false, T, kk, EP, H, I, p.lanes_down, p.cost_split) <= lds_bytes;
 }
@@ -156,6 +161,15 @@ int plan_check(const Plan& p, int64_t T, int top_k, int E, int shared, int H, in
   if (p.combine_in_down &&
       (p.ffn != MOE_FFN_GEMV || p.shared_mfma || !down_fold_ok(T, top_k + shared, I, p.lanes_down,
                                                                  kGfx950LdsBytes)))
+    return MOE_ERR_UNSUPPORTED;
+  if (p.one_launch != 0 && p.one_launch != 1) return MOE_ERR_INVALID_ARG;
+  // the one-launch FFN: the GEMV routing inside gate/up, no shared expert, an
+  // even split, a separate combine, both stages' LDS within the device's
+  if (p.one_launch &&
+      (p.ffn != MOE_FFN_GEMV || p.route != MOE_ROUTE_IN_GATE_UP || shared || p.cost_split ||
+       p.combine_in_down ||
+       one_launch_min_lds(T, top_k + shared, E, H, I, p.lanes_gate_up, p.lanes_down) >
+           kGfx950LdsBytes))
     return MOE_ERR_UNSUPPORTED;
   if (p.shared_mfma && !shared) return MOE_ERR_INVALID_ARG;
   // the shared expert's matrix-core workgroups: with the GEMV, up to 32 rows

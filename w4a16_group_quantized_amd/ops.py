@@ -61,7 +61,7 @@ class Plan(ctypes.Structure):
                 ("lanes_gate_up", ctypes.c_int32), ("lanes_down", ctypes.c_int32),
                 ("rows_per_pass", ctypes.c_int32), ("cost_split", ctypes.c_int32),
                 ("router_gemv", ctypes.c_int32), ("shared_mfma", ctypes.c_int32),
-                ("combine_in_down", ctypes.c_int32)]
+                ("combine_in_down", ctypes.c_int32), ("one_launch", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
