@@ -84,7 +84,7 @@ extern "C" {
 /* Static, NUL-terminated description of a return code (host only). */
 const char* moe_status_string(int status);
 
-/* Library ABI version, MAJOR * 100 + MINOR. */
+/* Library ABI version, MAJOR * 100 + MINOR (1.02: moe_plan gained one_launch). */
 int moe_abi_version(void);
 
 /*

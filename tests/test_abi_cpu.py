@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = ops.load_library()
-    assert lib.moe_abi_version() == 101
+    assert lib.moe_abi_version() == 102
     for st in range(5):
         assert len(ops.status_string(st)) > 0
     assert ops.status_string(99) == "unknown status"

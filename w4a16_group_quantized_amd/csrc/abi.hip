@@ -166,7 +166,7 @@ const char* moe_status_string(int status) {
   }
 }
 
-int moe_abi_version(void) { return 101; }
+int moe_abi_version(void) { return 102; }
 
 int moe_route(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t* topk_ids,
               float* topk_weights, void* stream) {
