@@ -761,13 +761,9 @@ __global__ __launch_bounds__(kFoldThreads) void down_fold_kernel(DecodeArgs p, G
   const int n_active = *p.num_active;
   const int n = b * R + k;
   const uint32_t row = n < H ? static_cast<uint32_t>(n) : static_cast<uint32_t>(H);  // past: zeros
-  for (int a = wave; a < n_active; a += kFoldWaves) {
-    const int e = p.active[a];
-    const int r0 = p.offsets[e];
-    const int nr = min(2, p.offsets[e + 1] - r0);
+  // a unit (one active expert's block): its loads, then its sums
+  auto issue = [&](int e, Slot (&sl)[kFoldMaxSpb], uint32_t (&sh)[kFoldMaxSpb]) {
     const ExpertBufs bufs = expert_bufs(p, H, G, e);
-    Slot sl[kFoldMaxSpb];
-    uint32_t sh[kFoldMaxSpb];
 #pragma unroll
     for (int j = 0; j < kFoldMaxSpb; ++j) {
       if (j < spb) {
@@ -777,6 +773,10 @@ __global__ __launch_bounds__(kFoldThreads) void down_fold_kernel(DecodeArgs p, G
             bufs.s, static_cast<int>((row * static_cast<uint32_t>(G) + gg) * 2u), 0, 0);
       }
     }
+  };
+  auto finish = [&](int e, const Slot (&sl)[kFoldMaxSpb], const uint32_t (&sh)[kFoldMaxSpb]) {
+    const int r0 = p.offsets[e];
+    const int nr = min(2, p.offsets[e + 1] - r0);
     float acc0 = 0.f, acc1 = 0.f;
     const uint32_t* f0 = frags + static_cast<size_t>(r0) * 2 * G * kFragDwords;
     const uint32_t* f1 = f0 + 2 * G * kFragDwords;
@@ -807,6 +807,20 @@ __global__ __launch_bounds__(kFoldThreads) void down_fold_kernel(DecodeArgs p, G
         ybuf[(r0 + 1) * R + k] = v1;
       }
     }
+  };
+  // Experts a and a + kFoldWaves together: the second one's loads are out
+  // before the first one's sums (10 experts over 8 waves at 1 token: two
+  // waves hold two, and their second expert no longer waits on the first).
+  for (int a = wave; a < n_active; a += 2 * kFoldWaves) {
+    const bool two = a + kFoldWaves < n_active;
+    const int e = p.active[a];
+    const int e2 = p.active[two ? a + kFoldWaves : a];
+    Slot sl[kFoldMaxSpb], sl2[kFoldMaxSpb];
+    uint32_t sh[kFoldMaxSpb], sh2[kFoldMaxSpb];
+    issue(e, sl, sh);
+    if (two) issue(e2, sl2, sh2);
+    finish(e, sl, sh);
+    if (two) finish(e2, sl2, sh2);
   }
   __syncthreads();
   for (int i = static_cast<int>(threadIdx.x); i < p.T * R; i += kFoldThreads) {
